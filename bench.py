@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is one pass of the whole device path for one batch and one attention layer:
+copy-on-write block copies (when the workload has any), the cache write of each sequence's new
+token, the per-partition decode kernel and the partition merge. The block manager runs on the
+host at set-up (its per-step cost is timed separately and reported as host_manager_us_per_step).
+
+Default workload: 256 sequences, 32 query / 8 KV heads, head_dim 128, block 16, bf16, a
+512-token prefix shared by every sequence (32 physical blocks, refcount 256) and a private
+suffix of uniform length on [64, 3584]. Inputs are synthetic (seeded) and resident in HBM
+before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: value = KV-read GB/s over the distinct KV bytes the step must read
+(a shared block counts once), plus decode tokens/s, the roofline of the decode kernel (bytes
+per launch over its HIP-event duration) and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
+    p.add_argument("--partition", type=int, default=512)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain block copy of known size (HBM counter calibration)")
+    return p.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# workload set-up through the block manager
+# ---------------------------------------------------------------------------------------------
+
+def build_state(name, pk, gen, torch, dev):
+    maker = gen.WORKLOADS[name]
+    case = maker(values=False)
+    B, bs, W = case.num_seqs, case.block_size, case.table_width
+    lens = case.seq_lens.astype(np.int64)
+    # free order that makes the manager hand out exactly the generated placement
+    order, seen = [], set()
+    for b in range(B):
+        for j in range(-(-int(lens[b]) // bs)):
+            x = int(case.block_tables[b, j])
+            if x not in seen:
+                seen.add(x)
+                order.append(x)
+    order += [x for x in range(case.num_blocks) if x not in seen]
+    bm = pk.BlockManager(case.num_blocks, bs, np.array(order, np.int32))
+    prefix_tokens = case.meta.get("prefix_tokens", 0)
+    if prefix_tokens:
+        owner = -1
+        bm.add_seq(owner, prefix_tokens)
+        for b in range(B):
+            bm.share_prefix(owner, b, prefix_tokens // bs)
+            bm.extend(b, int(lens[b]) - prefix_tokens)
+        bm.free_seq(owner)
+    else:
+        for b in range(B):
+            bm.add_seq(b, int(lens[b]))
+    tables, seq_lens = bm.build_tables(range(B), W)
+    assert np.array_equal(tables, case.block_tables) and np.array_equal(seq_lens, case.seq_lens)
+    # the token written this step is the last one each sequence attends to
+    slots = np.array([bm.slots(b, int(lens[b]) - 1, 1)[0] for b in range(B)], np.int32)
+    shape = (case.num_blocks, case.num_kv_heads, bs, case.head_dim)
+    seed = 402100
+    st = {
+        "case": case, "bm": bm,
+        "k": gen.device_normal(shape, case.dtype, seed, dev),
+        "v": gen.device_normal(shape, case.dtype, seed + 1, dev),
+        "q": gen.device_normal((B, case.num_q_heads, case.head_dim), case.dtype, seed + 2, dev),
+        "k_new": gen.device_normal((B, case.num_kv_heads, case.head_dim), case.dtype, seed + 3, dev),
+        "v_new": gen.device_normal((B, case.num_kv_heads, case.head_dim), case.dtype, seed + 4, dev),
+        "tables": torch.from_numpy(tables).to(dev),
+        "lens": torch.from_numpy(seq_lens).to(dev),
+        "slots": torch.from_numpy(slots).to(dev),
+        "pairs": None,
+    }
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+    st["out"] = torch.empty((B, case.num_q_heads, case.head_dim), dtype=tdt, device=dev)
+    return st
+
+
+def host_manager_cost(pk, case, iters=20):
+    """Host microseconds per decode step of the block manager: one append per sequence plus the
+    padded table export, on a private manager holding the same lengths."""
+    B, bs = case.num_seqs, case.block_size
+    lens = case.seq_lens.astype(np.int64)
+    width = case.table_width + iters // bs + 2
+    bm = pk.BlockManager(case.num_blocks + B * (iters // bs + 2), bs)
+    prefix = case.meta.get("prefix_tokens", 0)
+    if prefix:
+        bm.add_seq(-1, prefix)
+    for b in range(B):
+        if prefix:
+            bm.share_prefix(-1, b, prefix // bs)
+            bm.extend(b, int(lens[b]) - prefix)
+        else:
+            bm.add_seq(b, int(lens[b]))
+    ids = np.arange(B, dtype=np.int64)
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        bm.append_slots(ids)
+        bm.build_tables(ids, width)
+    return (time.perf_counter() - t0) / iters * 1e6
+
+
+# ---------------------------------------------------------------------------------------------
+# algorithmic bytes
+# ---------------------------------------------------------------------------------------------
+
+def byte_model(case, part):
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    B, Hq, D, bs = case.num_seqs, case.num_q_heads, case.head_dim, case.block_size
+    lens = case.seq_lens.astype(np.int64)
+    kv_tok = case.kv_bytes_per_token()
+    unique = kv_tok * case.unique_slots()
+    logical = kv_tok * int(lens.sum())
+    nparts = np.maximum(1, -(-lens // part))
+    multi = nparts > 1
+    tables = 4 * int((-(-lens // bs)).sum())
+    q = B * Hq * D * eb
+    partial_rows = int((nparts * multi).sum()) * Hq
+    partials = partial_rows * (D + 2) * 4
+    out_single = int((~multi).sum()) * Hq * D * eb
+    out_all = B * Hq * D * eb
+    decode_kernel = unique + q + tables + 4 * B + partials + out_single
+    reduce_kernel = partials + out_all - out_single
+    cache_write = 2 * 2 * B * case.num_kv_heads * D * eb    # read new rows, write slots
+    return {"kv_unique": unique, "kv_logical": logical, "decode_kernel": decode_kernel,
+            "reduce_kernel": reduce_kernel, "cache_write": cache_write,
+            "partitions": int(nparts.sum()), "multi_partition_seqs": int(multi.sum())}
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ---------------------------------------------------------------------------------------------
+
+def cpu_baseline(st, target_s, gen):
+    from oracle import paged_attention as opa
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl absent: numpy's default is one BLAS pool
+        blas_threads = os.cpu_count() or 1
+    import torch
+    case = st["case"]
+    dt, bs = case.dtype, case.block_size
+    kv_tok = case.kv_bytes_per_token()
+
+    def host(t):
+        t = t.cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+    spent, done, seen = 0.0, 0, {}
+    for b in range(case.num_seqs):
+        L = int(case.seq_lens[b])
+        nb = -(-L // bs)
+        ids = case.block_tables[b, :nb]
+        idx = torch.from_numpy(ids.astype(np.int64)).to(st["k"].device)
+        ksub, vsub = host(st["k"][idx]), host(st["v"][idx])
+        q = host(st["q"][b:b + 1])
+        table = np.arange(nb, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        opa.decode_attention(q, ksub, vsub, table, np.array([L], np.int32), case.scale, dt)
+        spent += time.perf_counter() - t0
+        done += 1
+        for j, blk in enumerate(ids.tolist()):
+            seen[blk] = max(seen.get(blk, 0), min(bs, L - j * bs))
+        if spent >= target_s:
+            break
+    uniq_bytes = kv_tok * sum(seen.values())
+    return {"value": round(uniq_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": "fp64 numpy oracle over the first %d of %d sequences (all %d query heads), "
+                      "%.1f s; GB/s over the sample's distinct KV bytes; host %s, %d logical CPUs"
+                      % (done, case.num_seqs, case.num_q_heads, spent, platform.processor() or
+                         platform.machine(), len(os.sched_getaffinity(0))),
+            "seconds": round(spent, 3), "tokens_per_s": round(done / spent, 3)}
+
+
+# ---------------------------------------------------------------------------------------------
+
+def copy_probe(pk, torch, dev):
+    """A plain copy of known size through copy_blocks: 4096 blocks of 64 KiB per cache, read
+    once and written once (512 MiB each way), repeated 5 times."""
+    nb, H, bs, D = 8192, 8, 16, 128
+    k = torch.zeros((nb, H, bs, D), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(0, 4096), torch.arange(4096, 8192)], 1).to(torch.int32).to(dev)
+    for _ in range(5):
+        pk.copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    per = 2 * 4096 * H * bs * D * 2
+    print(json.dumps({"copy_probe": True, "bytes_read_per_launch": per,
+                      "bytes_written_per_launch": per, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), flush=True)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_402_amd as pk
+    from workloads import gen
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(pk, torch, dev)
+        return
+
+    log("setting up %s" % args.workload)
+    st = build_state(args.workload, pk, gen, torch, dev)
+    case = st["case"]
+    part = args.partition
+    bytes_ = byte_model(case, part)
+    ws = torch.empty(max(1, pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads,
+                                                      case.table_width, case.block_size,
+                                                      case.head_dim, part)),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+
+    def step(i=None):
+        if st["pairs"] is not None:
+            pk.copy_blocks(st["k"], st["v"], st["pairs"])
+        if i is not None:
+            ev[i][0].record()
+        pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
+        if i is not None:
+            ev[i][1].record()
+        pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
+                                      st["lens"], case.scale, partition_size=part, workspace=ws)
+        if i is not None:
+            ev[i][2].record()
+        pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width, ws,
+                                  partition_size=part)
+        if i is not None:
+            ev[i][3].record()
+
+    log("warmup %d" % W)
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % K)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    t_cw = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_dec = [e[1].elapsed_time(e[2]) for e in ev]
+    t_red = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    dec_ms = float(np.mean(t_dec))
+    gbps = bytes_["kv_unique"] / (ms_step * 1e-3) / 1e9
+    achieved = bytes_["decode_kernel"] / (dec_ms * 1e-3) / 1e9
+    log("step %.4f ms, decode kernel %.4f ms (p10 %.4f, p90 %.4f), reduce %.4f ms, cache write "
+        "%.4f ms" % (ms_step, dec_ms, np.percentile(t_dec, 10), np.percentile(t_dec, 90), t_red,
+                     t_cw))
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/Q on the device; seeded lengths and placement)",
+        "config": {"workload": case.name, "num_seqs": case.num_seqs,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size,
+                   "kv_dtype": case.dtype, "partition_size": part,
+                   "prefix_tokens": case.meta.get("prefix_tokens", 0),
+                   "mean_seq_len": round(float(case.seq_lens.mean()), 1),
+                   "num_blocks": case.num_blocks, "parallelism": "single GPU"},
+        "decode_tokens_per_s": round(case.num_seqs / (ms_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "kv_unique_bytes": bytes_["kv_unique"],
+        "kv_logical_bytes": bytes_["kv_logical"],
+        "effective_logical_GBps": round(bytes_["kv_logical"] / (ms_step * 1e-3) / 1e9, 2),
+        "kernel_ms": {"decode_partitions": round(dec_ms, 5), "partition_reduce": round(t_red, 5),
+                      "reshape_and_cache": round(t_cw, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "paged_decode_partition_kernel",
+                     "bytes_per_launch": bytes_["decode_kernel"]},
+    }
+    log("host manager cost")
+    result["host_manager_us_per_step"] = round(host_manager_cost(pk, case), 1)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, about %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds, gen)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: decode attention over a paged KV cache on MI355X
+ * (gfx950), the cache-write and block-copy kernels it relies on, and a host block manager.
+ *
+ * Pages cited (all three describe vLLM's PagedAttention):
+ *   P1 = openeuler.csdn.net/6ae29ebb40858c2d88170ea6.html (explainer, sections 1-9)
+ *   P2 = agent.csdn.net/6a744dae662f9a54cb99003e.html (article, sections 1-5)
+ *   P3 = aiknowledge.cn "2.2 PagedAttention 与 KV Cache 分页管理" (sections 2.2.1-2.2.13)
+ *
+ * ------------------------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ------------------------------------------------------------------------------------------
+ *  - Every call returns an int status (PKV_OK or a negative PKV_E* code) and never throws.
+ *    pkv_last_error() returns a thread-local message describing the last failure.
+ *  - Device calls take device pointers owned by the caller, enqueue work on `stream`
+ *    (a hipStream_t; NULL = the null stream) and never synchronise. Shapes, dtypes and
+ *    alignment are checked on the host before any launch (PKV_EINVAL / PKV_EDTYPE); launch
+ *    failures return PKV_EHIP.
+ *  - The contents of device index arrays (table entries, seq_lens, slots, pairs) are not
+ *    checked on the host (that would need a device->host copy). Every kernel bounds-checks
+ *    them on the device instead and skips an out-of-range entry (a table entry outside
+ *    [0, num_blocks), a slot outside [0, num_blocks*block_size), a pair outside the pool), so
+ *    bad indices never address memory outside the caller's buffers. Results for such inputs
+ *    are unspecified.
+ *  - The library allocates no device memory. Split-K partials live in a caller-provided
+ *    workspace of pkv_decode_workspace_bytes() bytes.
+ *  - Data types: PKV_F32 (IEEE binary32), PKV_F16 (IEEE binary16), PKV_BF16 (bfloat16).
+ *    All arithmetic is fp32; conversion to a 16-bit output rounds to nearest, ties to even.
+ *
+ * ------------------------------------------------------------------------------------------
+ * KV pool layout (P1 §4.1; P2 §2.1; P3 §2.2.2: fixed-size blocks, 16 tokens by default)
+ * ------------------------------------------------------------------------------------------
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim], row-major, separate
+ *                      buffers of the same dtype. The tile of one (block, KV head) is
+ *                      block_size*head_dim*elem_bytes contiguous bytes (4 KiB for block 16,
+ *                      head_dim 128, bf16), so one token row is head_dim*elem_bytes contiguous
+ *                      bytes that lanes read as 16-byte vectors.
+ *   slot s           : physical block s / block_size, offset s % block_size (P3 §2.2.3).
+ *   block_tables     : int32 [num_seqs][max_blocks_per_seq]; entry [b][j] is the physical
+ *                      block holding tokens j*block_size .. (j+1)*block_size-1 of sequence b
+ *                      (P1 §4.2; P3 §2.2.3). Entries at j >= ceil(seq_len/block_size) are
+ *                      never read (padding, -1 by convention). Several rows may list the same
+ *                      physical block (prefix sharing, P1 §6.1; P3 §2.2.3).
+ *   seq_lens         : int32 [num_seqs]; tokens cached for each sequence, including the token
+ *                      written by this step's pkv_reshape_and_cache. Values above
+ *                      max_blocks_per_seq*block_size are clamped to it; negatives act as 0.
+ * Limits: head_dim in {64, 128, 256}; block_size a power of two in [8, 256];
+ *         num_q_heads / num_kv_heads in {1, 2, 4, 8}; num_blocks*block_size < 2^31;
+ *         head_dim*elem_bytes a multiple of 128; 16-byte aligned q/out/caches.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,      /* bad shape, size, pointer or argument */
+  PKV_EDTYPE = -2,      /* unsupported dtype combination */
+  PKV_ENOBLOCKS = -3,   /* block manager: the fixed pool cannot meet the request */
+  PKV_EHIP = -4,        /* a HIP launch or runtime call failed */
+  PKV_ENOSEQ = -5,      /* block manager: unknown sequence id */
+  PKV_EWORKSPACE = -6   /* workspace missing or smaller than pkv_decode_workspace_bytes() */
+};
+
+/* Library version (major*10000 + minor*100 + patch). */
+int pkv_version(void);
+
+/* Thread-local text of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ==========================================================================================
+ * Device operations
+ * ========================================================================================== */
+
+/* Bytes of split-K workspace pkv_paged_attention_decode needs: for every (sequence, query
+ * head, context partition) one running max, one exponent sum and one head_dim-long fp32
+ * accumulator. partition_size defaults to 512 when 0 is passed. Returns 0 on bad input. */
+size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
+                                  int block_size, int head_dim, int partition_size);
+
+/* Decode attention over the paged cache (P1 §4.2; P2 §3.1; P3 §2.2.4: the kernel reads
+ * KV block by block through the block table).
+ *   out[b][h][:] = sum_t softmax_t(scale * q[b][h].k_t) v_t
+ * over the seq_lens[b] cached tokens t of sequence b, where k_t and v_t are row t % block_size
+ * of KV head h / (num_q_heads/num_kv_heads) in physical block block_tables[b][t / block_size].
+ * A sequence of length 0 produces a zero row.
+ *   out          : [num_seqs][num_q_heads][head_dim] of out_dtype (kv_dtype or PKV_F32)
+ *   q            : [num_seqs][num_q_heads][head_dim] of kv_dtype
+ *   scale        : softmax scale (usually 1/sqrt(head_dim))
+ *   partition_size: tokens per context partition (split-K); a multiple of 32 and of
+ *                  block_size in [32, 2048]; 0 selects 512. Sequences longer than one
+ *                  partition are finished by a second, deterministic merge pass.
+ *   workspace    : device buffer of at least pkv_decode_workspace_bytes() bytes; may be NULL
+ *                  only if workspace_bytes is 0 and no sequence can span two partitions
+ *                  (max_blocks_per_seq*block_size <= partition_size).
+ * The output is a deterministic function of the inputs: it does not depend on where the
+ * blocks sit in the pool, nor on which other sequences share them. */
+int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                               const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, float scale, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two passes of pkv_paged_attention_decode, exposed separately so a caller can time or
+ * schedule them apart. Same arguments and results as the combined call:
+ *   _partitions: one workgroup per (KV head, sequence, partition) attends over its partition;
+ *                single-partition sequences get their final row in `out`, others leave
+ *                (max, sum, accumulator) partials in the workspace.
+ *   _reduce    : for sequences with more than one partition, merges the partials in
+ *                partition order into `out`. */
+int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, const void* k_cache,
+                                   const void* v_cache, int kv_dtype,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, int max_blocks_per_seq,
+                                   float scale, int partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int partition_size,
+                               const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cache write (P1 §4.3; P3 §2.2.2-§2.2.3): token t's K and V rows ([num_kv_heads][head_dim],
+ * contiguous, t-major) are copied bit for bit to slot slot_mapping[t] of k_cache / v_cache.
+ * A negative slot skips the token. Slots must be distinct. */
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          int dtype, const int32_t* slot_mapping, int num_tokens,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          void* stream);
+
+/* Copy-on-write block copy (P1 §6.2; P2 §2.2): for each (src, dst) pair of the int32
+ * [num_pairs][2] array, block dst of both caches (all KV heads, all slots) becomes a bit
+ * copy of block src. dst values must be distinct and disjoint from every src. */
+int pkv_copy_blocks(void* k_cache, void* v_cache, int dtype, const int32_t* src_dst_pairs,
+                    int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, void* stream);
+
+/* ==========================================================================================
+ * Host block manager (P2 §3.1 manager sketch; P1 §4.1-§4.3, §6; P3 §2.2.2-§2.2.3)
+ * A fixed pool of num_blocks blocks; a per-sequence block table; a refcount per block. Host
+ * memory only, owned by the handle. Not thread-safe: one thread per handle at a time.
+ * Failing calls change no state (PKV_ENOBLOCKS also counts one allocation failure).
+ * ========================================================================================== */
+typedef struct pkv_bm pkv_bm;
+
+/* free_order: NULL (ids 0,1,2,... in that order) or a permutation of [0, num_blocks) giving
+ * the order in which blocks are handed out. Freed blocks are handed out again last-freed
+ * first; a freed sequence releases its last logical block first. Returns NULL on bad input. */
+pkv_bm* pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* New sequence holding num_tokens tokens in ceil(num_tokens/block_size) fresh blocks. */
+int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int num_tokens);
+
+/* child gets parent's table and length; every listed block's refcount grows by one
+ * (parallel sampling / beam branches share the parent's blocks, P2 §2.2). */
+int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child);
+
+/* New sequence dst whose table is the first num_prefix_blocks (full) blocks of src, shared
+ * (P1 §6.1; P3 §2.2.3 key point). Its length is num_prefix_blocks*block_size. */
+int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int64_t dst, int num_prefix_blocks);
+
+/* Reserves the slot of the sequence's next token (its current length becomes the position).
+ * Position % block_size == 0: a fresh block is appended (P3 §2.2.3). Otherwise the token
+ * goes into the last block; if that block is shared (refcount > 1) it is first replaced by a
+ * fresh private block whose contents the caller must copy from *cow_src to *cow_dst with
+ * pkv_copy_blocks before writing (P1 §6.2). Returns 0 (no copy), 1 (copy needed) or <0. */
+int pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src,
+                       int32_t* cow_dst);
+
+/* pkv_bm_append_slot for n sequences in order, atomically: on failure every append of the
+ * batch is undone. slots: int32[n]; cow_pairs: int32[n][2] receives the copies needed, in
+ * order; *num_cow their count. */
+int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                        int32_t* cow_pairs, int* num_cow);
+
+/* Appends num_tokens tokens to the sequence, as that many pkv_bm_append_slot calls in a row
+ * (prefill of a new chunk), atomically: on failure nothing changes. At most the first token
+ * can need a copy-on-write; *cow_src / *cow_dst (may be NULL) receive it, or -1. The slots
+ * of the new tokens are available from pkv_bm_slots. Returns 0, 1 (copy needed) or <0. */
+int pkv_bm_extend(pkv_bm* bm, int64_t seq, int num_tokens, int32_t* cow_src, int32_t* cow_dst);
+
+/* Releases the sequence: every block's refcount drops by one; blocks reaching zero return
+ * to the free pool (P3 §2.2.2). */
+int pkv_bm_free_seq(pkv_bm* bm, int64_t seq);
+
+/* Copies up to cap entries of the sequence's table to out; *num_tokens (if not NULL) gets
+ * its length. Returns the number of blocks in the table, or <0. */
+int pkv_bm_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* num_tokens);
+
+/* Slots of token positions [start, start+count) of the sequence (all < its length). */
+int pkv_bm_slots(const pkv_bm* bm, int64_t seq, int start, int count, int32_t* out);
+
+/* Padded int32 [n][width] block tables (-1 past each table's end) and int32 seq_lens[n] for
+ * the listed sequences, ready for pkv_paged_attention_decode. Fails if a table is wider. */
+int pkv_bm_build_tables(const pkv_bm* bm, const int64_t* seqs, int n, int32_t* tables,
+                        int width, int32_t* seq_lens);
+
+/* Refcount of one block (0 = free), or <0 for an id outside the pool. */
+int pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+
+/* Counters for pool monitoring (P3 §2.2.13 asks for pool occupancy and allocation
+ * failures): out[0] blocks in use, [1] free blocks, [2] shared blocks (refcount > 1),
+ * [3] copy-on-write copies issued, [4] allocation failures, [5] live sequences,
+ * [6] reserved (0), [7] reserved (0). */
+int pkv_bm_stats(const pkv_bm* bm, int64_t out[8]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -115,6 +115,29 @@ class BlockManagerModel:
         self.seqs[seq][1] = n + 1
         return status, blk * self.block_size + off, cs, cd
 
+    def extend(self, seq, num_tokens):
+        """num_tokens appends in a row, all or nothing. Returns (status, cow_src, cow_dst) of
+        the first append (the only one that can copy)."""
+        if seq not in self.seqs:
+            return ENOSEQ, -1, -1
+        if num_tokens < 0:
+            return EINVAL, -1, -1
+        saved = (list(self.free), list(self.rc), list(self.seqs[seq][0]), self.seqs[seq][1],
+                 self.cow_copies)
+        first = (OK, -1, -1)
+        for i in range(num_tokens):
+            st, _, cs, cd = self.append_slot(seq)
+            if st < 0:
+                failures = self.alloc_failures
+                self.free, self.rc = saved[0], saved[1]
+                self.seqs[seq] = [saved[2], saved[3]]
+                self.cow_copies = saved[4]
+                self.alloc_failures = failures
+                return st, -1, -1
+            if i == 0:
+                first = (st, cs, cd)
+        return first
+
     def free_seq(self, seq):
         if seq not in self.seqs:
             return ENOSEQ

@@ -1,0 +1,15 @@
+"""MI355X-native decode attention over a paged KV cache.
+
+    from paged_kv_cache_402_amd import (paged_attention_decode, reshape_and_cache, copy_blocks,
+                                        BlockManager)
+
+The device operations run in hand-written HIP kernels for gfx950 inside libpagedkv.so (C ABI in
+include/pagedkv.h); the block manager is C++ in the same library. Importing fails loudly if the
+library has not been built (python paged_kv_cache_402_amd/build.py).
+"""
+from ._lib import PagedKVError, lib, last_error  # noqa: F401  (raises if the library is missing)
+from .block_manager import BlockManager  # noqa: F401
+from .ops import (copy_blocks, decode_workspace_bytes, paged_attention_decode,  # noqa: F401
+                  paged_attention_partitions, paged_attention_reduce, reshape_and_cache)
+
+__version__ = "0.1.0"

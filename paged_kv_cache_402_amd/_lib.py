@@ -1,0 +1,87 @@
+"""ctypes loader of libpagedkv.so: argument and result types of every exported symbol.
+
+The library is built in-tree (python paged_kv_cache_402_amd/build.py). There is no fallback:
+if the library is missing, importing this module raises.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+c_int, c_int64, c_size_t, c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+c_void_p, c_char_p = ctypes.c_void_p, ctypes.c_char_p
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+P_i64 = ctypes.POINTER(ctypes.c_int64)
+P_int = ctypes.POINTER(ctypes.c_int)
+
+# name -> (restype, argtypes); mirrors include/pagedkv.h
+SIGNATURES = {
+    "pkv_version": (c_int, []),
+    "pkv_last_error": (c_char_p, []),
+    "pkv_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "pkv_paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                           c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                           c_int, c_int, c_float, c_int, c_void_p, c_size_t,
+                                           c_void_p]),
+    "pkv_paged_attention_partitions": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                               c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                               c_int, c_int, c_int, c_int, c_float, c_int,
+                                               c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attention_reduce": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
+                                           c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_reshape_and_cache": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                      c_int, c_int, c_int, c_int, c_int, c_void_p]),
+    "pkv_copy_blocks": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
+                                c_int, c_void_p]),
+    "pkv_bm_create": (c_void_p, [c_int, c_int, P_i32]),
+    "pkv_bm_destroy": (None, [c_void_p]),
+    "pkv_bm_add_seq": (c_int, [c_void_p, c_int64, c_int]),
+    "pkv_bm_fork": (c_int, [c_void_p, c_int64, c_int64]),
+    "pkv_bm_share_prefix": (c_int, [c_void_p, c_int64, c_int64, c_int]),
+    "pkv_bm_append_slot": (c_int, [c_void_p, c_int64, P_i32, P_i32, P_i32]),
+    "pkv_bm_append_slots": (c_int, [c_void_p, P_i64, c_int, P_i32, P_i32, P_int]),
+    "pkv_bm_extend": (c_int, [c_void_p, c_int64, c_int, P_i32, P_i32]),
+    "pkv_bm_free_seq": (c_int, [c_void_p, c_int64]),
+    "pkv_bm_table": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),
+    "pkv_bm_slots": (c_int, [c_void_p, c_int64, c_int, c_int, P_i32]),
+    "pkv_bm_build_tables": (c_int, [c_void_p, P_i64, c_int, P_i32, c_int, P_i32]),
+    "pkv_bm_refcount": (c_int, [c_void_p, ctypes.c_int32]),
+    "pkv_bm_stats": (c_int, [c_void_p, P_i64]),
+}
+
+# status codes (include/pagedkv.h)
+PKV_OK, PKV_EINVAL, PKV_EDTYPE, PKV_ENOBLOCKS, PKV_EHIP, PKV_ENOSEQ, PKV_EWORKSPACE = (
+    0, -1, -2, -3, -4, -5, -6)
+STATUS_NAMES = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EDTYPE", -3: "PKV_ENOBLOCKS",
+                -4: "PKV_EHIP", -5: "PKV_ENOSEQ", -6: "PKV_EWORKSPACE"}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code, where, message):
+        super().__init__("%s failed with %s: %s" % (where, STATUS_NAMES.get(code, code), message))
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpagedkv.so is not built; run `python paged_kv_cache_402_amd/build.py` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return (lib.pkv_last_error() or b"").decode(errors="replace")
+
+
+def check(code: int, where: str) -> int:
+    if code < 0:
+        raise PagedKVError(code, where, last_error())
+    return code

@@ -1,0 +1,323 @@
+// Host block manager: a fixed pool of equal-size KV blocks, one block table per sequence,
+// a refcount per block, on-demand growth, fork / prefix sharing and copy-on-write.
+//
+// Pages cited:
+//   P1 = openeuler.csdn.net/6ae29ebb40858c2d88170ea6.html (explainer, sections 1-9)
+//   P2 = agent.csdn.net/6a744dae662f9a54cb99003e.html (article, sections 1-5)
+//   P3 = aiknowledge.cn "2.2 PagedAttention 与 KV Cache 分页管理" (sections 2.2.1-2.2.13)
+//
+// What the pages fix: any free block can serve any request (P1 §4.1); a table maps logical
+// to physical blocks (P1 §4.2; P3 §2.2.3); a block is added only when the last one is full
+// and nothing moves on growth (P1 §4.3; P3 §2.2.3); finished or preempted sequences return
+// their blocks (P3 §2.2.2); tables may share physical blocks (P1 §6.1; P3 §2.2.3); a write
+// into a shared block copies only that block (P1 §6.2; P2 §2.2).
+// Readings taken where they are silent: the pool is fixed (the pseudo-code on P2 §3.1 grows
+// it; here an unmet request fails with PKV_ENOBLOCKS and changes nothing); "shared" means
+// refcount > 1 and the last holder writes in place; free blocks form a LIFO stack seeded by
+// a caller-given order, so results are reproducible id for id.
+#include <cstdint>
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+
+#include "errors.h"
+#include "pagedkv.h"
+
+struct pkv_bm {
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int64_t tokens = 0;
+  };
+  int num_blocks = 0;
+  int block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> rc;          // refcount per block; 0 = free
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t shared = 0;               // blocks with rc > 1
+  int64_t cow_copies = 0;
+  int64_t alloc_failures = 0;
+
+  void inc(int32_t b) {
+    if (++rc[b] == 2) ++shared;
+  }
+  void dec(int32_t b) {
+    if (rc[b]-- == 2) --shared;
+    if (rc[b] == 0) free_stack.push_back(b);
+  }
+  int32_t take() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    rc[b] = 1;
+    return b;
+  }
+  // Returns a block taken last back to the top of the free stack.
+  void untake(int32_t b) {
+    rc[b] = 0;
+    free_stack.push_back(b);
+  }
+};
+
+namespace {
+
+// What one append changed, so a failed batch can be rolled back exactly.
+struct AppendUndo {
+  pkv_bm::Seq* seq;
+  int kind;         // 0: wrote in place, 1: fresh block appended, 2: copy-on-write
+  int32_t src, dst;
+};
+
+int append_one(pkv_bm* bm, int64_t id, int32_t* slot, AppendUndo* undo) {
+  auto it = bm->seqs.find(id);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "append_slot: unknown sequence %lld", (long long)id);
+  pkv_bm::Seq& s = it->second;
+  const int bs = bm->block_size;
+  if (s.tokens >= (int64_t)INT32_MAX) return pkv::fail(PKV_EINVAL, "append_slot: sequence too long");
+  const int off = (int)(s.tokens % bs);
+  int32_t blk;
+  undo->seq = &s;
+  undo->src = undo->dst = -1;
+  if (off == 0) {
+    if (bm->free_stack.empty()) {
+      ++bm->alloc_failures;
+      return pkv::fail(PKV_ENOBLOCKS, "append_slot: pool exhausted");
+    }
+    blk = bm->take();
+    s.blocks.push_back(blk);
+    undo->kind = 1;
+    undo->dst = blk;
+  } else {
+    int32_t last = s.blocks.back();
+    if (bm->rc[last] > 1) {
+      if (bm->free_stack.empty()) {
+        ++bm->alloc_failures;
+        return pkv::fail(PKV_ENOBLOCKS, "append_slot: pool exhausted (copy-on-write)");
+      }
+      blk = bm->take();
+      bm->dec(last);  // stays > 0: it was shared
+      s.blocks.back() = blk;
+      ++bm->cow_copies;
+      undo->kind = 2;
+      undo->src = last;
+      undo->dst = blk;
+    } else {
+      blk = last;
+      undo->kind = 0;
+    }
+  }
+  ++s.tokens;
+  *slot = blk * bs + off;
+  return undo->kind == 2 ? 1 : 0;
+}
+
+void undo_one(pkv_bm* bm, const AppendUndo& u) {
+  pkv_bm::Seq& s = *u.seq;
+  --s.tokens;
+  if (u.kind == 1) {
+    s.blocks.pop_back();
+    bm->untake(u.dst);
+  } else if (u.kind == 2) {
+    s.blocks.back() = u.src;
+    bm->inc(u.src);
+    bm->untake(u.dst);
+    --bm->cow_copies;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_bm* pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order) {
+  if (num_blocks <= 0 || block_size <= 0 || (int64_t)num_blocks * block_size >= INT32_MAX) {
+    pkv::fail(PKV_EINVAL, "bm_create: bad pool size");
+    return nullptr;
+  }
+  pkv_bm* bm = new pkv_bm();
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->rc.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  std::vector<char> seen(num_blocks, 0);
+  for (int i = 0; i < num_blocks; ++i) {
+    int32_t b = free_order ? free_order[i] : i;
+    if (b < 0 || b >= num_blocks || seen[b]) {
+      delete bm;
+      pkv::fail(PKV_EINVAL, "bm_create: free_order is not a permutation of the pool");
+      return nullptr;
+    }
+    seen[b] = 1;
+    bm->free_stack[num_blocks - 1 - i] = b;  // order[0] on top
+  }
+  pkv::ok();
+  return bm;
+}
+
+void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int num_tokens) {
+  if (!bm || num_tokens < 0) return pkv::fail(PKV_EINVAL, "add_seq: bad argument");
+  if (bm->seqs.count(seq)) return pkv::fail(PKV_EINVAL, "add_seq: sequence %lld exists", (long long)seq);
+  size_t need = ((size_t)num_tokens + bm->block_size - 1) / bm->block_size;
+  if (need > bm->free_stack.size()) {
+    ++bm->alloc_failures;
+    return pkv::fail(PKV_ENOBLOCKS, "add_seq: %zu blocks needed, %zu free", need, bm->free_stack.size());
+  }
+  pkv_bm::Seq s;
+  s.blocks.reserve(need + 1);
+  for (size_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+  s.tokens = num_tokens;
+  bm->seqs.emplace(seq, std::move(s));
+  return pkv::ok();
+}
+
+int pkv_bm_fork(pkv_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return pkv::fail(PKV_EINVAL, "fork: null manager");
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "fork: unknown parent %lld", (long long)parent);
+  if (bm->seqs.count(child)) return pkv::fail(PKV_EINVAL, "fork: child %lld exists", (long long)child);
+  pkv_bm::Seq s = it->second;
+  for (int32_t b : s.blocks) bm->inc(b);
+  bm->seqs.emplace(child, std::move(s));
+  return pkv::ok();
+}
+
+int pkv_bm_share_prefix(pkv_bm* bm, int64_t src, int64_t dst, int num_prefix_blocks) {
+  if (!bm || num_prefix_blocks < 0) return pkv::fail(PKV_EINVAL, "share_prefix: bad argument");
+  auto it = bm->seqs.find(src);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "share_prefix: unknown source %lld", (long long)src);
+  if (bm->seqs.count(dst)) return pkv::fail(PKV_EINVAL, "share_prefix: %lld exists", (long long)dst);
+  if ((int64_t)num_prefix_blocks * bm->block_size > it->second.tokens)
+    return pkv::fail(PKV_EINVAL, "share_prefix: only full blocks can be shared");
+  pkv_bm::Seq s;
+  s.blocks.assign(it->second.blocks.begin(), it->second.blocks.begin() + num_prefix_blocks);
+  s.tokens = (int64_t)num_prefix_blocks * bm->block_size;
+  for (int32_t b : s.blocks) bm->inc(b);
+  bm->seqs.emplace(dst, std::move(s));
+  return pkv::ok();
+}
+
+int pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  if (!bm || !slot) return pkv::fail(PKV_EINVAL, "append_slot: bad argument");
+  AppendUndo u;
+  int st = append_one(bm, seq, slot, &u);
+  if (st < 0) return st;
+  if (cow_src) *cow_src = u.kind == 2 ? u.src : -1;
+  if (cow_dst) *cow_dst = u.kind == 2 ? u.dst : -1;
+  pkv::ok();
+  return st;
+}
+
+int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                        int32_t* cow_pairs, int* num_cow) {
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_cow)
+    return pkv::fail(PKV_EINVAL, "append_slots: bad argument");
+  std::vector<AppendUndo> log(n);
+  int ncow = 0;
+  for (int i = 0; i < n; ++i) {
+    int st = append_one(bm, seqs[i], &slots[i], &log[i]);
+    if (st < 0) {
+      for (int j = i - 1; j >= 0; --j) undo_one(bm, log[j]);
+      return st;
+    }
+    if (st == 1) {
+      cow_pairs[2 * ncow] = log[i].src;
+      cow_pairs[2 * ncow + 1] = log[i].dst;
+      ++ncow;
+    }
+  }
+  *num_cow = ncow;
+  return pkv::ok();
+}
+
+int pkv_bm_extend(pkv_bm* bm, int64_t seq, int num_tokens, int32_t* cow_src, int32_t* cow_dst) {
+  if (!bm || num_tokens < 0) return pkv::fail(PKV_EINVAL, "extend: bad argument");
+  if (!bm->seqs.count(seq)) return pkv::fail(PKV_ENOSEQ, "extend: unknown sequence %lld", (long long)seq);
+  std::vector<AppendUndo> log((size_t)num_tokens);
+  int first = 0;
+  int32_t slot;
+  for (int i = 0; i < num_tokens; ++i) {
+    int st = append_one(bm, seq, &slot, &log[i]);
+    if (st < 0) {
+      for (int j = i - 1; j >= 0; --j) undo_one(bm, log[j]);
+      return st;
+    }
+    if (i == 0) first = st;
+  }
+  if (cow_src) *cow_src = first == 1 ? log[0].src : -1;
+  if (cow_dst) *cow_dst = first == 1 ? log[0].dst : -1;
+  pkv::ok();
+  return first;
+}
+
+int pkv_bm_free_seq(pkv_bm* bm, int64_t seq) {
+  if (!bm) return pkv::fail(PKV_EINVAL, "free_seq: null manager");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "free_seq: unknown sequence %lld", (long long)seq);
+  const std::vector<int32_t>& blocks = it->second.blocks;
+  for (size_t i = blocks.size(); i-- > 0;) bm->dec(blocks[i]);
+  bm->seqs.erase(it);
+  return pkv::ok();
+}
+
+int pkv_bm_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* num_tokens) {
+  if (!bm || cap < 0 || (cap > 0 && !out)) return pkv::fail(PKV_EINVAL, "table: bad argument");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "table: unknown sequence %lld", (long long)seq);
+  const auto& s = it->second;
+  int n = (int)s.blocks.size();
+  std::memcpy(out, s.blocks.data(), sizeof(int32_t) * (size_t)(n < cap ? n : cap));
+  if (num_tokens) *num_tokens = (int)s.tokens;
+  pkv::ok();
+  return n;
+}
+
+int pkv_bm_slots(const pkv_bm* bm, int64_t seq, int start, int count, int32_t* out) {
+  if (!bm || start < 0 || count < 0 || (count > 0 && !out)) return pkv::fail(PKV_EINVAL, "slots: bad argument");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "slots: unknown sequence %lld", (long long)seq);
+  const auto& s = it->second;
+  if ((int64_t)start + count > s.tokens) return pkv::fail(PKV_EINVAL, "slots: positions past the sequence end");
+  const int bs = bm->block_size;
+  for (int i = 0; i < count; ++i) {
+    int t = start + i;
+    out[i] = s.blocks[t / bs] * bs + t % bs;
+  }
+  return pkv::ok();
+}
+
+int pkv_bm_build_tables(const pkv_bm* bm, const int64_t* seqs, int n, int32_t* tables, int width,
+                        int32_t* seq_lens) {
+  if (!bm || n < 0 || width <= 0 || (n > 0 && (!seqs || !tables || !seq_lens)))
+    return pkv::fail(PKV_EINVAL, "build_tables: bad argument");
+  for (int i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "build_tables: unknown sequence %lld", (long long)seqs[i]);
+    const auto& s = it->second;
+    if ((int)s.blocks.size() > width) return pkv::fail(PKV_EINVAL, "build_tables: table wider than %d", width);
+    int32_t* row = tables + (size_t)i * width;
+    std::memcpy(row, s.blocks.data(), sizeof(int32_t) * s.blocks.size());
+    for (int j = (int)s.blocks.size(); j < width; ++j) row[j] = -1;
+    seq_lens[i] = (int32_t)s.tokens;
+  }
+  return pkv::ok();
+}
+
+int pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return pkv::fail(PKV_EINVAL, "refcount: bad block");
+  return bm->rc[block];
+}
+
+int pkv_bm_stats(const pkv_bm* bm, int64_t out[8]) {
+  if (!bm || !out) return pkv::fail(PKV_EINVAL, "stats: bad argument");
+  out[0] = bm->num_blocks - (int64_t)bm->free_stack.size();
+  out[1] = (int64_t)bm->free_stack.size();
+  out[2] = bm->shared;
+  out[3] = bm->cow_copies;
+  out[4] = bm->alloc_failures;
+  out[5] = (int64_t)bm->seqs.size();
+  out[6] = 0;
+  out[7] = 0;
+  return pkv::ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,267 @@
+// C ABI of the device operations: host-side validation, workspace layout and dispatch to the
+// gfx950 kernels. Nothing here touches device memory contents or synchronises.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "errors.h"
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+constexpr size_t kMaxDecodeLds = 64 * 1024;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+int elem_bytes(int dt) { return dt == PKV_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct DecodePlan {
+  DecodeArgs args;
+  int group;
+  size_t ws_needed;
+};
+
+int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const void* k_cache,
+                const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                int partition_size, void* workspace, size_t workspace_bytes) {
+  if (!dtype_ok(kv_dtype)) return fail(PKV_EDTYPE, "decode: unknown kv dtype %d", kv_dtype);
+  if (out_dtype != kv_dtype && out_dtype != PKV_F32)
+    return fail(PKV_EDTYPE, "decode: out dtype must equal the kv dtype or be fp32");
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "decode: num_seqs %d out of range", num_seqs);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "decode: query heads must be a positive multiple of kv heads");
+  const int group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PKV_EINVAL, "decode: query heads per kv head must be 1, 2, 4 or 8 (got %d)", group);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PKV_EINVAL, "decode: head_dim must be 64, 128 or 256");
+  if (head_dim == 256 && group == 8) return fail(PKV_EINVAL, "decode: head_dim 256 supports groups up to 4");
+  if ((head_dim * elem_bytes(kv_dtype)) % 128 != 0) return fail(PKV_EINVAL, "decode: row bytes must be a multiple of 128");
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_EINVAL, "decode: block_size must be a power of two in [8, 256]");
+  if (num_blocks <= 0 || (int64_t)num_blocks * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "decode: num_blocks out of range");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "decode: max_blocks_per_seq out of range");
+  if (partition_size == 0) partition_size = 512;
+  if (partition_size < 32 || partition_size > 2048 || partition_size % 32 != 0 || partition_size % block_size != 0)
+    return fail(PKV_EINVAL, "decode: partition_size must be a multiple of 32 and of block_size in [32, 2048]");
+  if (decode_lds_bytes(kv_dtype, head_dim, group, partition_size) > kMaxDecodeLds)
+    return fail(PKV_EINVAL, "decode: partition_size too large for LDS at this group size");
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int64_t pmax = (max_tokens + partition_size - 1) / partition_size;
+  if (pmax > kMaxGridYZ) return fail(PKV_EINVAL, "decode: too many partitions per sequence");
+  if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "decode: null pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_EINVAL, "decode: q and caches must be 16-byte aligned");
+  size_t need = 0;
+  if (pmax > 1) need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+
+  DecodeArgs& a = pl->args;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.ws_ml = reinterpret_cast<float*>(workspace);
+  a.ws_acc = need ? a.ws_ml + (size_t)num_seqs * num_q_heads * (size_t)pmax * 2 : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.bs_log2 = log2i(block_size);
+  a.part = partition_size;
+  a.pmax = (int)pmax;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.out_dtype = out_dtype;
+  pl->group = group;
+  pl->ws_needed = need;
+  return ok();
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
+                                  int block_size, int head_dim, int partition_size) {
+  if (partition_size == 0) partition_size = 512;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
+      head_dim <= 0 || partition_size <= 0)
+    return 0;
+  const int64_t pmax = ((int64_t)max_blocks_per_seq * block_size + partition_size - 1) / partition_size;
+  if (pmax <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+}
+
+int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, const void* k_cache,
+                                   const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                   int max_blocks_per_seq, float scale, int partition_size,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
+                    "decode partitions launch");
+}
+
+int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int partition_size, const void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (out_dtype != PKV_F32 && out_dtype != PKV_F16 && out_dtype != PKV_BF16)
+    return fail(PKV_EDTYPE, "reduce: unknown out dtype %d", out_dtype);
+  if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0) return fail(PKV_EINVAL, "reduce: bad sizes");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return fail(PKV_EINVAL, "reduce: bad head_dim");
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256) return fail(PKV_EINVAL, "reduce: bad block_size");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "reduce: max_blocks_per_seq out of range");
+  if (partition_size == 0) partition_size = 512;
+  if (partition_size < 32 || partition_size > 2048 || partition_size % 32 != 0 || partition_size % block_size != 0)
+    return fail(PKV_EINVAL, "reduce: bad partition_size");
+  const int64_t pmax = ((int64_t)max_blocks_per_seq * block_size + partition_size - 1) / partition_size;
+  if (pmax <= 1 || num_seqs == 0) return ok();  // nothing spans two partitions
+  if (pmax > 65535) return fail(PKV_EINVAL, "reduce: too many partitions per sequence");
+  const size_t need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EWORKSPACE, "reduce: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!out || !seq_lens) return fail(PKV_EINVAL, "reduce: null pointer");
+  DecodeArgs a = {};
+  a.out = out;
+  a.seq_lens = seq_lens;
+  a.ws_ml = (float*)workspace;
+  a.ws_acc = a.ws_ml + (size_t)num_seqs * num_q_heads * (size_t)pmax * 2;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.bs_log2 = log2i(block_size);
+  a.part = partition_size;
+  a.pmax = (int)pmax;
+  a.out_dtype = out_dtype;
+  return hip_status(launch_decode_reduce(a, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                               const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, float scale, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
+                  "decode partitions launch");
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache, int dtype,
+                          const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, void* stream) {
+  if (!dtype_ok(dtype)) return fail(PKV_EDTYPE, "reshape_and_cache: unknown dtype %d", dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "reshape_and_cache: bad sizes");
+  const int64_t row_bytes = (int64_t)head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0) return fail(PKV_EINVAL, "reshape_and_cache: head_dim*elem_bytes must be a multiple of 16");
+  if ((int64_t)num_kv_heads * row_bytes / 16 > 65535LL * 256)
+    return fail(PKV_EINVAL, "reshape_and_cache: token rows too large");
+  if (!is_pow2(block_size) || block_size > 256) return fail(PKV_EINVAL, "reshape_and_cache: block_size must be a power of two <= 256");
+  if (num_blocks <= 0 || (int64_t)num_blocks * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "reshape_and_cache: num_blocks out of range");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PKV_EINVAL, "reshape_and_cache: null pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_EINVAL, "reshape_and_cache: buffers must be 16-byte aligned");
+  CacheWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.row_bytes = (int)row_bytes;
+  a.bs_log2 = log2i(block_size);
+  a.num_blocks = num_blocks;
+  return hip_status(launch_reshape_and_cache(a, (hipStream_t)stream), "reshape_and_cache launch");
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, int dtype, const int32_t* src_dst_pairs,
+                    int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    void* stream) {
+  if (!dtype_ok(dtype)) return fail(PKV_EDTYPE, "copy_blocks: unknown dtype %d", dtype);
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_EINVAL, "copy_blocks: bad sizes");
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return fail(PKV_EINVAL, "copy_blocks: block bytes must be a multiple of 16");
+  if ((block_bytes / 16 + 4095) / 4096 > 65535) return fail(PKV_EINVAL, "copy_blocks: blocks too large");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !src_dst_pairs) return fail(PKV_EINVAL, "copy_blocks: null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PKV_EINVAL, "copy_blocks: caches must be 16-byte aligned");
+  CopyBlocksArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.pairs = src_dst_pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.block_bytes = block_bytes;
+  return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "copy_blocks launch");
+}
+
+}  // extern "C"

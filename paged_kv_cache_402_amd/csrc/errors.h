@@ -1,0 +1,14 @@
+// Thread-local error text behind pkv_last_error().
+#pragma once
+
+#include <cstdarg>
+
+namespace pkv {
+
+// Formats the message (printf-style), stores it for pkv_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Clears the stored message; returns PKV_OK.
+int ok();
+
+}  // namespace pkv

@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI (capi.cpp) and the kernels (*.hip).
+// Arguments here are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Workgroup shape of the decode kernel: 4 waves of 64 lanes.
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = 4;
+
+struct DecodeArgs {
+  void* out;                   // [B][Hq][D] of out dtype
+  const void* q;               // [B][Hq][D] of kv dtype
+  const void* k_cache;         // [NB][Hkv][bs][D]
+  const void* v_cache;
+  const int32_t* block_tables; // [B][max_blocks]
+  const int32_t* seq_lens;     // [B]
+  float* ws_ml;                // [B][Hq][pmax][2]: running max (log2 units) and exponent sum
+  float* ws_acc;               // [B][Hq][pmax][D]: unnormalised accumulators
+  int num_seqs, num_q_heads, num_kv_heads, num_blocks, max_blocks;
+  int bs_log2;                 // log2(block_size)
+  int part;                    // tokens per partition
+  int pmax;                    // partitions of the longest representable sequence
+  float scale_log2;            // scale * log2(e): scores are kept in base-2 units
+  int out_dtype;               // DType of out
+};
+
+// Bytes of dynamic LDS one decode workgroup needs.
+size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part);
+
+// Launches the per-partition kernel (grid: Hkv x B x pmax).
+hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_dim, int group,
+                                    hipStream_t stream);
+// Launches the partition merge (grid: Hq x B); only multi-partition sequences do work.
+hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream);
+
+struct CacheWriteArgs {
+  const void* k;            // [T][Hkv][D]
+  const void* v;
+  void* k_cache;            // [NB][Hkv][bs][D]
+  void* v_cache;
+  const int32_t* slots;     // [T]
+  int num_tokens, num_kv_heads, row_bytes, bs_log2, num_blocks;
+};
+hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
+
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* pairs;     // [n][2]
+  int num_pairs, num_blocks;
+  int64_t block_bytes;      // bytes of one block of one cache (all heads, all slots)
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
+}  // namespace pkv

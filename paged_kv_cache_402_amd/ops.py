@@ -1,0 +1,160 @@
+"""Python face of the device operations: argument marshalling only.
+
+Each function reads shapes from torch tensors, checks dtypes/devices/contiguity, and calls the
+C ABI with raw device pointers on torch's current HIP stream. All computation happens in the
+HIP kernels of libpagedkv.so; nothing here computes on the host or falls back to torch ops.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import lib, check
+
+KV_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DEFAULT_PARTITION = 512
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a device (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _i32(t: torch.Tensor, name: str):
+    _dev(t, name)
+    if t.dtype != torch.int32:
+        raise ValueError("%s must be int32" % name)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _kv_dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in KV_DTYPES:
+        raise ValueError("%s must be float32, float16 or bfloat16" % name)
+    return KV_DTYPES[t.dtype]
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                           block_size: int, head_dim: int,
+                           partition_size: int = DEFAULT_PARTITION) -> int:
+    return int(lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, max_blocks_per_seq,
+                                              block_size, head_dim, partition_size))
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens):
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected q [B][Hq][D] and caches [NB][Hkv][bs][D] of equal shape")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or out.shape != q.shape:
+        raise ValueError("head_dim mismatch between q, out and the caches")
+    kdt = _kv_dtype(k_cache, "k_cache")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    if out.dtype not in (k_cache.dtype, torch.float32):
+        raise ValueError("out must have the cache dtype or float32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables [B][W] and seq_lens [B] expected")
+    return B, Hq, D, NB, Hkv, bs, kdt, KV_DTYPES[out.dtype], block_tables.shape[1]
+
+
+def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
+    need = decode_workspace_bytes(B, Hq, W, bs, D, partition_size)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
+                           partition_size: int = DEFAULT_PARTITION, workspace=None):
+    """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
+    b's block table locates in the paged caches. Returns `out`."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    check(lib.pkv_paged_attention_decode(
+        out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+        partition_size, ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_decode")
+    return out
+
+
+def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
+                               partition_size: int = DEFAULT_PARTITION, workspace=None):
+    """First pass of paged_attention_decode only (per-partition attention). Returns the
+    workspace that paged_attention_reduce needs (None if no sequence spans two partitions)."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    check(lib.pkv_paged_attention_partitions(
+        out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+        partition_size, ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_partitions")
+    return ws
+
+
+def paged_attention_reduce(out, seq_lens, block_size, max_blocks_per_seq, workspace,
+                           partition_size: int = DEFAULT_PARTITION):
+    """Second pass of paged_attention_decode only: merges the partitions' partials into out."""
+    _dev(out, "out")
+    _i32(seq_lens, "seq_lens")
+    B, Hq, D = out.shape
+    odt = _kv_dtype(out, "out")
+    if workspace is None:
+        wsp, wsb = None, 0
+    else:
+        _dev(workspace, "workspace")
+        wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib.pkv_paged_attention_reduce(out.data_ptr(), odt, seq_lens.data_ptr(), B, Hq, D,
+                                         block_size, max_blocks_per_seq, partition_size, wsp,
+                                         wsb, _stream(out)), "paged_attention_reduce")
+    return out
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping):
+    """Stores token t's K/V rows ([Hkv][D] each) at slot slot_mapping[t] of the caches
+    (bit copy; negative slots are skipped)."""
+    for t, n in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    _i32(slot_mapping, "slot_mapping")
+    if k.dim() != 3 or k.shape != v.shape or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("expected k, v [T][Hkv][D] and caches [NB][Hkv][bs][D]")
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv, D) != (Hkv2, D2) or slot_mapping.shape != (T,):
+        raise ValueError("k/v rows do not match the cache layout or slot_mapping length")
+    dt = _kv_dtype(k_cache, "k_cache")
+    if not (k.dtype == v.dtype == v_cache.dtype == k_cache.dtype):
+        raise ValueError("k, v and the caches must share a dtype")
+    check(lib.pkv_reshape_and_cache(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), dt, slot_mapping.data_ptr(), T, Hkv, D,
+                                    bs, NB, _stream(k)), "reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs):
+    """For each (src, dst) row of the int32 [n][2] tensor, block dst of both caches becomes a
+    bit copy of block src."""
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache")
+    _i32(src_dst_pairs, "src_dst_pairs")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or k_cache.dim() != 4:
+        raise ValueError("caches must share shape [NB][Hkv][bs][D] and dtype")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n][2]")
+    NB, Hkv, bs, D = k_cache.shape
+    check(lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(),
+                              _kv_dtype(k_cache, "k_cache"), src_dst_pairs.data_ptr(),
+                              src_dst_pairs.shape[0], Hkv, D, bs, NB, _stream(k_cache)),
+          "copy_blocks")

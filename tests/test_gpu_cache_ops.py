@@ -1,0 +1,214 @@
+"""GPU bit-exactness of the cache write and block copy, and whole decode steps driven by the
+C++ block manager against the oracle's independent path (MI355X only).
+
+Pages cited:
+  P1 = openeuler.csdn.net/6ae29ebb40858c2d88170ea6.html
+  P2 = agent.csdn.net/6a744dae662f9a54cb99003e.html
+  P3 = aiknowledge.cn "2.2 PagedAttention 与 KV Cache 分页管理"
+
+The product side runs: C++ manager -> copy_blocks -> reshape_and_cache -> decode (HIP).
+The oracle side runs: Python manager model -> reference copy -> reference cache write ->
+fp64 attention. They share only the generated inputs.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cache_ops as ref_ops
+from oracle.block_manager_model import BlockManagerModel
+from workloads import gen
+from tests.gpu_util import GATE, i32, max_err, oracle, run_decode, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_402_amd  # noqa: F401
+
+
+def pk():
+    import paged_kv_cache_402_amd
+    return paged_kv_cache_402_amd
+
+
+def _bits_equal(dev, host, dtype):
+    return np.array_equal(to_host(dev, dtype).view(np.uint8), np.ascontiguousarray(host).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reshape_and_cache_bit_exact(dtype, d):
+    rng = np.random.default_rng(3 + d)
+    nb, H, bs = 64, 4, 16
+    kc = gen.normal(rng, (nb, H, bs, d), dtype)
+    vc = gen.normal(rng, (nb, H, bs, d), dtype)
+    T = 200
+    slots = rng.choice(nb * bs, T, replace=False).astype(np.int32)
+    slots[::17] = -1
+    kn = gen.normal(rng, (T, H, d), dtype)
+    vn = gen.normal(rng, (T, H, d), dtype)
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    pk().reshape_and_cache(to_dev(kn, dtype), to_dev(vn, dtype), kd, vd, i32(slots))
+    torch.cuda.synchronize()
+    kr, vr = ref_ops.reshape_and_cache(kn, vn, kc, vc, slots)
+    assert _bits_equal(kd, kr, dtype) and _bits_equal(vd, vr, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_copy_blocks_bit_exact(dtype):
+    rng = np.random.default_rng(4)
+    nb, H, bs, d = 80, 8, 32, 128
+    kc = gen.normal(rng, (nb, H, bs, d), dtype)
+    vc = gen.normal(rng, (nb, H, bs, d), dtype)
+    kc[5, :, 3:] = gen.nan_value(dtype)   # NaN payloads are copied as bits too
+    ids = rng.permutation(nb)
+    pairs = np.stack([ids[:20], ids[20:40]], axis=1).astype(np.int32)
+    pairs[0, 0] = 5
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    pk().copy_blocks(kd, vd, i32(pairs))
+    torch.cuda.synchronize()
+    kr, vr = ref_ops.copy_blocks(kc, vc, pairs)
+    assert _bits_equal(kd, kr, dtype) and _bits_equal(vd, vr, dtype)
+
+
+def test_copy_blocks_skips_pairs_outside_the_pool():
+    rng = np.random.default_rng(5)
+    kc = gen.normal(rng, (8, 2, 16, 64), "f32")
+    kd, vd = to_dev(kc, "f32"), to_dev(kc.copy(), "f32")
+    pk().copy_blocks(kd, vd, i32([[1, 2], [9, 3], [4, -1]]))
+    torch.cuda.synchronize()
+    kr, _ = ref_ops.copy_blocks(kc, kc, [[1, 2]])
+    assert _bits_equal(kd, kr, "f32")
+
+
+def _hash_blocks(pool_dev, dtype):
+    h = to_host(pool_dev, dtype)
+    return [hashlib.sha256(np.ascontiguousarray(h[b]).tobytes()).hexdigest() for b in range(h.shape[0])]
+
+
+def test_tiny_decode_step_with_cow():
+    """Four sequences (1, 15, 16, 35 tokens; the last one on blocks 7, 3, 9 as in P3 §2.2.3):
+    decode, write one token each (the 16-token sequence opens a new block), decode again, then
+    fork the 36-token sequence and append to the child: its shared last block is copied first
+    (P1 §6.2), the source block is unchanged and the sibling's output does not change."""
+    P = pk()
+    case = gen.tiny_case(pin_worked_example=True)
+    bm = P.BlockManager(32, 16, case.free_order)
+    model = BlockManagerModel(32, 16, case.free_order)
+    for s, L in enumerate(case.seq_lens.tolist()):
+        bm.add_seq(s, L)
+        model.add_seq(s, L)
+    tables, lens = bm.build_tables(range(4), 4)
+    assert np.array_equal(tables, case.block_tables) and np.array_equal(lens, case.seq_lens)
+    assert bm.table(3)[0] == [7, 3, 9]
+    kd, vd = to_dev(case.k_cache, "f32"), to_dev(case.v_cache, "f32")
+    got, _ = run_decode(case, k=kd, v=vd)
+    assert max_err(got, oracle(case)) <= GATE["f32"]
+
+    # one new token per sequence
+    slots, pairs = bm.append_slots([0, 1, 2, 3])
+    mres = [model.append_slot(s) for s in range(4)]
+    assert slots.tolist() == [r[1] for r in mres] and pairs.shape[0] == 0
+    assert slots[3] == 147                       # token 35 of the worked example
+    assert len(bm.table(2)[0]) == 2              # 16 tokens -> the 17th opens a block
+    k_new, v_new = case.meta["k_new"], case.meta["v_new"]
+    P.reshape_and_cache(to_dev(k_new, "f32"), to_dev(v_new, "f32"), kd, vd, i32(slots))
+    kc1, vc1 = ref_ops.reshape_and_cache(k_new, v_new, case.k_cache, case.v_cache,
+                                         [r[1] for r in mres])
+    torch.cuda.synchronize()
+    assert _bits_equal(kd, kc1, "f32") and _bits_equal(vd, vc1, "f32")
+    tables, lens = bm.build_tables(range(4), 4)
+    step2 = gen.PagedDecodeCase("tiny2", "f32", 4, 4, 64, 16, 32, lens, tables, case.scale,
+                                q=case.meta["q_next"], k_cache=kc1, v_cache=vc1)
+    got2, out2 = run_decode(step2, k=kd, v=vd)
+    ref2 = oracle(step2)
+    assert max_err(got2, ref2) <= GATE["f32"]
+
+    # fork the 36-token sequence, append to the child: copy-on-write of block 9
+    bm.fork(3, 4)
+    model.fork(3, 4)
+    before = _hash_blocks(kd, "f32")
+    slots_c, pairs_c = bm.append_slots([4])
+    st, slot_m, cs, cd = model.append_slot(4)
+    assert st == 1 and pairs_c.tolist() == [[cs, cd]] and cs == 9 and slots_c[0] == slot_m
+    assert bm.stats()["cow_copies"] == 1
+    P.copy_blocks(kd, vd, i32(pairs_c))
+    kn2 = gen.normal(np.random.default_rng(99), (1, 4, 64), "f32")
+    vn2 = gen.normal(np.random.default_rng(98), (1, 4, 64), "f32")
+    P.reshape_and_cache(to_dev(kn2, "f32"), to_dev(vn2, "f32"), kd, vd, i32(slots_c))
+    torch.cuda.synchronize()
+    after = _hash_blocks(kd, "f32")
+    changed = [b for b in range(32) if before[b] != after[b]]
+    assert changed == [cd]                        # only the private copy changed
+    kc2, vc2 = ref_ops.copy_blocks(kc1, vc1, [[cs, cd]])
+    kc2, vc2 = ref_ops.reshape_and_cache(kn2, vn2, kc2, vc2, [slot_m])
+    assert _bits_equal(kd, kc2, "f32") and _bits_equal(vd, vc2, "f32")
+    kh = to_host(kd, "f32")
+    assert np.array_equal(kh[cd, :, :4], kh[cs, :, :4])  # the copy holds the shared tokens
+
+    tables, lens = bm.build_tables(range(5), 4)
+    q5 = np.concatenate([case.meta["q_next"], case.meta["q_next"][3:4]])
+    step3 = gen.PagedDecodeCase("tiny3", "f32", 4, 4, 64, 16, 32, lens, tables, case.scale,
+                                q=q5, k_cache=kc2, v_cache=vc2)
+    got3, out3 = run_decode(step3, k=kd, v=vd)
+    assert max_err(got3, oracle(step3)) <= GATE["f32"]
+    assert torch.equal(out3[:4].cpu(), out2.cpu())   # siblings untouched, bit for bit
+
+
+def test_longtail_parallel_sampling_step():
+    """32 prompts x 4 branches, fp16, block 32, geometric lengths (mean 200): each branch
+    shares its prompt's blocks, appends one token (copy-on-write of the shared partial block
+    for 3 of the 4 branches, in place for the last), then decode over all 128 sequences."""
+    P = pk()
+    c = gen.llama13b_longtail_case()
+    nb, bs, H, d = c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim
+    bm = P.BlockManager(nb, bs, c.free_order)
+    model = BlockManagerModel(nb, bs, c.free_order)
+    host_k = np.full((nb, H, bs, d), gen.nan_value("f16"), dtype=np.float16)
+    host_v = host_k.copy()
+    kd, vd = to_dev(host_k, "f16"), to_dev(host_v, "f16")
+    B = c.num_seqs
+    for g, L in enumerate(c.decode_lens.tolist()):
+        parent = g * c.branches
+        bm.add_seq(parent, L - 1)
+        model.add_seq(parent, L - 1)
+        if L - 1 > 0:
+            s_dev = bm.slots(parent, 0, L - 1)
+            s_ref = model.slots(parent, 0, L - 1)
+            assert s_dev.tolist() == s_ref
+            P.reshape_and_cache(to_dev(c.prompt_k[g], "f16"), to_dev(c.prompt_v[g], "f16"), kd, vd,
+                                i32(s_dev))
+            host_k, host_v = ref_ops.reshape_and_cache(c.prompt_k[g], c.prompt_v[g], host_k,
+                                                       host_v, s_ref)
+        for br in range(1, c.branches):
+            bm.fork(parent, parent + br)
+            model.fork(parent, parent + br)
+    slots, pairs = bm.append_slots(range(B))
+    res = [model.append_slot(s) for s in range(B)]
+    assert slots.tolist() == [r[1] for r in res]
+    ref_pairs = [[r[2], r[3]] for r in res if r[0] == 1]
+    assert pairs.tolist() == ref_pairs
+    partial = sum(1 for L in c.decode_lens if (L - 1) % bs != 0)
+    assert len(ref_pairs) == 3 * partial
+    P.copy_blocks(kd, vd, i32(pairs.reshape(-1, 2)))
+    P.reshape_and_cache(to_dev(c.new_k, "f16"), to_dev(c.new_v, "f16"), kd, vd, i32(slots))
+    host_k, host_v = ref_ops.copy_blocks(host_k, host_v, ref_pairs)
+    host_k, host_v = ref_ops.reshape_and_cache(c.new_k, c.new_v, host_k, host_v,
+                                               [r[1] for r in res])
+    torch.cuda.synchronize()
+    assert _bits_equal(kd, host_k, "f16") and _bits_equal(vd, host_v, "f16")
+    tables, lens = bm.build_tables(range(B), c.table_width)
+    assert lens.tolist() == np.repeat(c.decode_lens, c.branches).tolist()
+    step = gen.PagedDecodeCase("longtail", "f16", H, H, d, bs, nb, lens, tables, c.scale, q=c.q,
+                               k_cache=host_k, v_cache=host_v)
+    got, _ = run_decode(step, k=kd, v=vd)
+    assert max_err(got, oracle(step)) <= GATE["f16"]
+    got16, _ = run_decode(step, k=kd, v=vd, out_dtype="f16")
+    ref = oracle(step)
+    from tests.gpu_util import half_ulp
+    assert (np.abs(got16 - ref) <= GATE["f16"] + half_ulp(ref, "f16")).all()

@@ -1,0 +1,290 @@
+"""GPU parity of the HIP decode path against the fp64 oracle (MI355X only).
+
+Pages cited:
+  P1 = openeuler.csdn.net/6ae29ebb40858c2d88170ea6.html
+  P2 = agent.csdn.net/6a744dae662f9a54cb99003e.html
+  P3 = aiknowledge.cn "2.2 PagedAttention 与 KV Cache 分页管理"
+
+Gates: max |HIP - oracle| <= 1e-5 (fp32 KV) or 2e-3 (fp16/bf16 KV) with fp32 output; with a
+16-bit output, the gate adds half an ulp of the output format at |oracle| (the rounding of the
+result itself). Pools hold NaN in every slot no sequence may read, so any stray read shows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import gen
+from tests.gpu_util import (GATE, half_ulp, i32, max_err, oracle, run_decode, to_dev, to_host,
+                            TORCH_DT)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_402_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _check(case, partition_size=512, out_dtype=None, seqs=None, ref=None):
+    got, _ = run_decode(case, out_dtype=out_dtype, partition_size=partition_size)
+    ref = oracle(case, seqs=seqs) if ref is None else ref
+    rows = slice(None) if seqs is None else list(seqs)
+    err = np.abs(got[rows] - ref[rows])
+    if out_dtype is None or out_dtype == "f32":
+        gate = GATE[case.dtype]
+    else:
+        gate = GATE[case.dtype] + half_ulp(ref[rows], out_dtype)
+    assert np.isfinite(got[rows]).all()
+    assert (err <= gate).all(), "max err %g" % float(err.max())
+    return got, ref
+
+
+# --------------------------------------------------------------------------------------------
+# the five workloads (reduced batch where the oracle would take long; full sizes sampled)
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pin", [False, True])
+def test_tiny_fp32(pin):
+    case = gen.tiny_case(pin_worked_example=pin)
+    if pin:
+        assert case.block_tables[3, :3].tolist() == [7, 3, 9]
+    _check(case)
+    _check(case, out_dtype="f32", partition_size=32)
+
+
+@pytest.mark.parametrize("out_dtype", [None, "bf16"])
+def test_llama2_7b_mha_reduced(out_dtype):
+    case = gen.llama2_7b_mha_case(num_seqs=6)
+    _check(case, out_dtype=out_dtype)
+
+
+def test_llama3_8b_gqa_prefix_reduced():
+    case = gen.llama3_8b_gqa_prefix_case(num_seqs=12)
+    got, ref = _check(case)
+    _check(case, out_dtype="bf16", ref=ref)
+
+
+def test_long_context_splitk_reduced():
+    case = gen.long_context_splitk_case(num_seqs=3, min_len=5000, max_len=20000)
+    _check(case)
+
+
+# --------------------------------------------------------------------------------------------
+# shapes, dtypes, block sizes, group sizes, partition sizes, ragged tails
+# --------------------------------------------------------------------------------------------
+
+LENS = [1, 2, 7, 8, 9, 31, 32, 33, 255, 511, 512, 513, 1000, 1024, 1025, 2100]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_shapes_and_groups(dtype, d, group):
+    if d == 256 and group == 8:
+        pytest.skip("head_dim 256 supports groups up to 4")
+    rng = np.random.default_rng(1000 + d + group)
+    hkv = 2
+    case = gen.make_case("shape", rng, LENS, hkv * group, hkv, d, 16, dtype)
+    _check(case)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 64, 128, 256])
+def test_block_sizes(bs):
+    rng = np.random.default_rng(bs)
+    part = max(512, bs)
+    case = gen.make_case("bs", rng, [1, bs - 1, bs, bs + 1, 3 * bs + 5, 1500], 8, 2, 128, bs,
+                         "bf16")
+    _check(case, partition_size=part)
+
+
+@pytest.mark.parametrize("part", [32, 64, 256, 512, 1024, 2048])
+def test_partition_sizes_agree(part):
+    rng = np.random.default_rng(77)
+    case = gen.make_case("part", rng, [1, 100, 700, 3000, 4500], 16, 4, 128, 16, "bf16")
+    _check(case, partition_size=part)
+
+
+def test_zero_length_and_single_token():
+    rng = np.random.default_rng(5)
+    case = gen.make_case("edge", rng, [0, 1, 0, 600], 4, 4, 128, 16, "f32")
+    got, out = run_decode(case)
+    assert (got[0] == 0).all() and (got[2] == 0).all()
+    # one token: exp(0) = 1, out = v exactly
+    blk = case.block_tables[1, 0]
+    assert np.array_equal(got[1], case.v_cache[blk, :, 0, :].astype(np.float64))
+    _check(case)
+
+
+def test_seq_lens_beyond_table_are_clamped():
+    rng = np.random.default_rng(6)
+    case = gen.make_case("clamp", rng, [48, 20], 4, 4, 64, 16, "f32", width=3)
+    lens_big = i32([10 ** 6, 20])
+    got, _ = run_decode(case, lens=lens_big)
+    clamped = gen.PagedDecodeCase(**{**case.__dict__, "seq_lens": np.array([48, 20], np.int32)})
+    ref = oracle(clamped)
+    assert max_err(got, ref) <= 1e-5
+
+
+def test_invalid_table_entries_are_skipped_without_faulting():
+    rng = np.random.default_rng(8)
+    case = gen.make_case("bad", rng, [40, 40], 4, 4, 128, 16, "bf16")
+    bad = case.block_tables.copy()
+    bad[0, 1] = case.num_blocks + 5     # out of the pool
+    bad[1, 0] = -7
+    got, _ = run_decode(case, tables=i32(bad))
+    # rows of sequences that only reference valid blocks are unaffected; the others are finite
+    assert np.isfinite(got).all()
+
+
+def test_scale_zero_gives_mean_of_values():
+    rng = np.random.default_rng(9)
+    case = gen.make_case("s0", rng, [37, 600], 8, 2, 128, 16, "f32")
+    case.scale = 0.0
+    _check(case)
+
+
+# --------------------------------------------------------------------------------------------
+# invariances the pages state, bit for bit on the device
+# --------------------------------------------------------------------------------------------
+
+def _scatter_logical(keys, bs, ids, num_blocks, dtype):
+    """[L][Hkv][d] rows -> pool with the rows placed through `ids` (test-side placement)."""
+    L, H, d = keys.shape
+    pool = np.full((num_blocks, H, bs, d), gen.nan_value(dtype), dtype=keys.dtype)
+    nb = -(-L // bs)
+    padded = np.full((nb * bs, H, d), gen.nan_value(dtype), dtype=keys.dtype)
+    padded[:L] = keys
+    pool[ids] = padded.reshape(nb, bs, H, d).transpose(0, 2, 1, 3)
+    return pool
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_placement_does_not_change_a_bit(dtype):
+    """P1 §4.2: the kernel sees the same logical sequence wherever its blocks sit."""
+    rng = np.random.default_rng(21)
+    bs, H, G, d = 16, 2, 4, 128
+    lens = [35, 700, 1500]
+    nbp = 400
+    keys = [gen.normal(rng, (L, H, d), dtype) for L in lens]
+    vals = [gen.normal(rng, (L, H, d), dtype) for L in lens]
+    q = to_dev(gen.normal(rng, (3, H * G, d), dtype), dtype)
+    outs = []
+    for trial in range(3):
+        perm = rng.permutation(nbp)
+        pos = 0
+        kpool = np.full((nbp, H, bs, d), gen.nan_value(dtype), dtype=keys[0].dtype)
+        vpool = np.full_like(kpool, gen.nan_value(dtype))
+        table = np.full((3, 100), -1, np.int32)
+        for s, L in enumerate(lens):
+            nb = -(-L // bs)
+            ids = perm[pos:pos + nb]
+            pos += nb
+            table[s, :nb] = ids
+            kp = _scatter_logical(keys[s], bs, ids, nbp, dtype)
+            vp = _scatter_logical(vals[s], bs, ids, nbp, dtype)
+            kpool[ids] = kp[ids]
+            vpool[ids] = vp[ids]
+        case = gen.PagedDecodeCase("perm", dtype, H * G, H, d, bs, nbp, np.array(lens, np.int32),
+                                   table, 0.09)
+        got, out = run_decode(case, q=q, k=to_dev(kpool, dtype), v=to_dev(vpool, dtype))
+        outs.append(out.cpu())
+        case.q, case.k_cache, case.v_cache = to_host(q, dtype), kpool, vpool
+        if trial == 0:
+            ref = oracle(case)
+            assert max_err(got, ref) <= GATE[dtype]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    """P3 §2.2.3 key point / P1 §6.1: sequences pointing at one set of prefix blocks get
+    exactly what they would get from private copies of those blocks."""
+    case = gen.llama3_8b_gqa_prefix_case(num_seqs=6)
+    got_shared, out_shared = run_decode(case)
+    prefix = case.meta["prefix_blocks"]
+    used = set(int(x) for x in case.block_tables.ravel() if x >= 0)
+    free = [b for b in range(case.num_blocks) if b not in used]
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    tables = case.block_tables.copy()
+    # sequences 1.. get their own copy of the prefix
+    pos = 0
+    for s in range(1, case.num_seqs):
+        for j, src in enumerate(prefix):
+            dst = free[pos]
+            pos += 1
+            kc[dst], vc[dst] = kc[src], vc[src]
+            tables[s, j] = dst
+    got_priv, out_priv = run_decode(case, k=to_dev(kc, "bf16"), v=to_dev(vc, "bf16"),
+                                    tables=i32(tables))
+    assert torch.equal(out_shared.cpu(), out_priv.cpu())
+    # equal queries over the prefix alone: identical rows
+    q_same = np.repeat(case.q[:1], case.num_seqs, axis=0)
+    lens = np.full(case.num_seqs, case.meta["prefix_tokens"], np.int32)
+    got_p, out_p = run_decode(case, q=to_dev(q_same, "bf16"), lens=i32(lens))
+    for s in range(1, case.num_seqs):
+        assert torch.equal(out_p[s].cpu(), out_p[0].cpu())
+
+
+def test_repeat_runs_are_bitwise_identical():
+    case = gen.long_context_splitk_case(num_seqs=2, min_len=3000, max_len=9000)
+    _, a = run_decode(case)
+    _, b = run_decode(case)
+    assert torch.equal(a.cpu(), b.cpu())
+
+
+# --------------------------------------------------------------------------------------------
+# full sizes in the benchmark's launch configuration, checked on sampled sequences
+# --------------------------------------------------------------------------------------------
+
+def _device_values(case, seed):
+    """Full-size pools from the device generator; the sampled sequences' blocks are copied
+    back for the oracle."""
+    dt = case.dtype
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    k = gen.device_normal(shape, dt, seed, "cuda")
+    v = gen.device_normal(shape, dt, seed + 1, "cuda")
+    q = gen.device_normal((case.num_seqs, case.num_q_heads, case.head_dim), dt, seed + 2, "cuda")
+    return q, k, v
+
+
+def _sampled_reference(case, q, k, v, seqs):
+    dt = case.dtype
+    bs = case.block_size
+    sub_tables, ids_all = [], []
+    for s in seqs:
+        nb = -(-int(case.seq_lens[s]) // bs)
+        ids_all.extend(case.block_tables[s, :nb].tolist())
+    uniq = sorted(set(ids_all))
+    remap = {b: i for i, b in enumerate(uniq)}
+    idx = torch.tensor(uniq, dtype=torch.long, device="cuda")
+    ksub, vsub = to_host(k[idx], dt), to_host(v[idx], dt)
+    width = case.block_tables.shape[1]
+    tab = np.full((len(seqs), width), -1, np.int32)
+    for r, s in enumerate(seqs):
+        nb = -(-int(case.seq_lens[s]) // bs)
+        tab[r, :nb] = [remap[int(b)] for b in case.block_tables[s, :nb]]
+    sub = gen.PagedDecodeCase("sample", dt, case.num_q_heads, case.num_kv_heads, case.head_dim, bs,
+                              len(uniq), case.seq_lens[list(seqs)], tab, case.scale,
+                              q=to_host(q[list(seqs)], dt), k_cache=ksub, v_cache=vsub)
+    return oracle(sub)
+
+
+@pytest.mark.parametrize("which", ["llama2_7b_mha", "llama3_8b_gqa_prefix", "long_context_splitk"])
+def test_full_size_sampled(which):
+    maker = gen.WORKLOADS[which]
+    case = maker(values=False)
+    q, k, v = _device_values(case, 4020)
+    got, out = run_decode(case, q=q, k=k, v=v)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(1)
+    nsamp = 2 if which == "long_context_splitk" else 6
+    seqs = sorted(rng.choice(case.num_seqs, nsamp, replace=False).tolist())
+    # always include the longest and the shortest sequence
+    seqs = sorted(set(seqs) | {int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))})
+    ref = _sampled_reference(case, q, k, v, seqs)
+    for r, s in enumerate(seqs):
+        assert max_err(got[s], ref[r]) <= GATE[case.dtype], "seq %d" % s
