@@ -28,8 +28,13 @@ template <> struct Elem<BF16> {
   static constexpr int per16 = 8;
 };
 
+// Reinterpretations take their operand by value: __builtin_bit_cast applied directly to an
+// element of an ext_vector lvalue (v[i]) reads element 0 whatever i is, so every vector
+// element is first copied into a scalar.
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -51,7 +56,7 @@ template <> __device__ __forceinline__ void widen<BF16>(const u32x4& v, float* f
 template <> __device__ __forceinline__ void widen<F16>(const u32x4& v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f16x2 h = __builtin_bit_cast(f16x2, v[i]);
+    const f16x2 h = as_f16x2(v[i]);
     f[2 * i] = (float)h[0];
     f[2 * i + 1] = (float)h[1];
   }
@@ -68,15 +73,13 @@ template <> __device__ __forceinline__ float dot16<F32>(const u32x4& q, const u3
 template <> __device__ __forceinline__ float dot16<BF16>(const u32x4& q, const u32x4& k, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]),
-                                          __builtin_bit_cast(bf16x2, k[i]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[i]), as_bf16x2(k[i]), acc, false);
   return acc;
 }
 template <> __device__ __forceinline__ float dot16<F16>(const u32x4& q, const u32x4& k, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]), __builtin_bit_cast(f16x2, k[i]),
-                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(as_f16x2(q[i]), as_f16x2(k[i]), acc, false);
   return acc;
 }
 

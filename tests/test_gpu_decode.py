@@ -206,18 +206,18 @@ def test_shared_prefix_equals_private_copies_bitwise():
     case = gen.llama3_8b_gqa_prefix_case(num_seqs=6)
     got_shared, out_shared = run_decode(case)
     prefix = case.meta["prefix_blocks"]
-    used = set(int(x) for x in case.block_tables.ravel() if x >= 0)
-    free = [b for b in range(case.num_blocks) if b not in used]
-    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    # sequences 1.. get their own copy of the prefix, in blocks appended past the pool
+    extra = (case.num_seqs - 1) * len(prefix)
+    pad = np.full((extra,) + case.k_cache.shape[1:], gen.nan_value("bf16"), dtype=np.uint16)
+    kc = np.concatenate([case.k_cache, pad])
+    vc = np.concatenate([case.v_cache, pad])
     tables = case.block_tables.copy()
-    # sequences 1.. get their own copy of the prefix
-    pos = 0
+    dst = case.num_blocks
     for s in range(1, case.num_seqs):
         for j, src in enumerate(prefix):
-            dst = free[pos]
-            pos += 1
             kc[dst], vc[dst] = kc[src], vc[src]
             tables[s, j] = dst
+            dst += 1
     got_priv, out_priv = run_decode(case, k=to_dev(kc, "bf16"), v=to_dev(vc, "bf16"),
                                     tables=i32(tables))
     assert torch.equal(out_shared.cpu(), out_priv.cpu())

@@ -402,3 +402,35 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                           to_f64(case.v_cache, "f32"), case.block_tables[0].tolist(), 5,
                           float(np.float32(0.7)), 2)
     assert np.max(np.abs(out[0] - ref)) > 1e-6
+
+
+def test_pins_catch_more_planted_mistakes(monkeypatch):
+    """A dropped scale and an off-by-one gather, planted in the oracle on the CPU, must each
+    fail a pin: the 50-digit brute force and the worked block-table example."""
+    rng = np.random.default_rng(11)
+    case = gen.make_case("bf2", rng, [6], 2, 1, 4, 4, "f32", scale=0.7)
+    ref = _brute_force_mp(to_f64(case.q, "f32")[0], to_f64(case.k_cache, "f32"),
+                          to_f64(case.v_cache, "f32"), case.block_tables[0].tolist(), 6,
+                          float(np.float32(0.7)), 2)
+    real_attend = pa.attend_one
+
+    def no_scale(q, keys, values, scale):
+        return real_attend(q, keys, values, 1.0)
+
+    monkeypatch.setattr(pa, "attend_one", no_scale)
+    out = pa.decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                              case.seq_lens, case.scale, "f32")
+    assert np.max(np.abs(out[0] - ref)) > 1e-6
+    monkeypatch.setattr(pa, "attend_one", real_attend)
+
+    g = golden()
+    pool = _slot_id_pool(16, 16)
+    real_gather = pa.gather_tokens
+
+    def shifted(cache, table_row, seq_len, kv_head):
+        # off by one token: row t read from position t + 1
+        rows = real_gather(cache, table_row, seq_len + 1, kv_head)
+        return rows[1:]
+
+    rows = shifted(pool, [7, 3, 9], 35, 0)
+    assert rows[:, 0].astype(int).tolist() != g["derived_by_hand"]["slots_of_tokens_0_to_34"]
