@@ -10,23 +10,34 @@
 // table and computes ordinary softmax attention of the new token's query over all of them.
 //
 // Work decomposition (our design for gfx950; the pages give no kernel structure):
-//   * one 256-lane workgroup per (KV head, sequence, context partition of `part` tokens);
-//     grid x is the KV head, so with 8 KV heads every workgroup of one head runs on the same
-//     XCD (workgroups are dealt to the 8 XCDs round-robin) and blocks shared by many
-//     sequences (a common prompt prefix) stay in that XCD's L2;
-//   * the G query rows of the GQA group are staged in LDS once, then held in registers;
-//   * K pass: 8 (or 16) lanes own one token row, each lane loads 16-byte vectors of it, takes
-//     the dot product with its slice of each query row (v_dot2 for 16-bit data), and a DPP
-//     butterfly inside the lane group finishes the sum; the scores of the partition go to LDS;
-//     the block id is resolved once per group of tokens from the table (a scalar load);
-//   * exact softmax inside the partition: max over the partition, then exp2 and the sum;
-//   * V pass: 16 lanes own one token row, each lane accumulates p * v for its 8 (or 4)
+//   * one 256-lane workgroup (4 waves) per (KV head, context partition of `part` tokens,
+//     sequence). Grid x is the KV head: workgroups are dealt to the 8 XCDs round-robin, so
+//     with 8 KV heads every workgroup of one head runs on one XCD and blocks shared by many
+//     sequences (a common prompt prefix) stay in that XCD's L2. Grid y is the partition and
+//     z the sequence, so the partitions of one sequence are dispatched together and the
+//     partitions that cover a shared prefix are spread over the whole launch instead of all
+//     running first;
+//   * each wave owns a quarter of the partition and works through it on its own: no
+//     workgroup barrier until the final merge, so the four waves never wait for each other
+//     and their loads stay in flight independently;
+//   * the partition's physical block ids are loaded once, one per lane, before any KV load;
+//     a step's id is then read with v_readlane, so no KV load waits on a table lookup;
+//   * K pass: LK lanes (8, or 16 for rows of more than 256 bytes) own one token row; each
+//     lane loads 16-byte vectors of it and takes the dot products with its slices of the G
+//     query rows of the GQA group (v_dot2 for 16-bit data, held in registers), finished by a
+//     DPP butterfly inside the lane group; UK steps of loads are issued before any use. The
+//     scores (in log2 units) go to the wave's own LDS area;
+//   * the wave's max, then 2^(s - max) once per (token, head) and the exponent sum; the
+//     first round of V loads is issued before this step so it overlaps it;
+//   * V pass: LV lanes (16) own one token row; each lane accumulates p * v for its 8 (or 4)
 //     columns and every head of the group in fp32;
-//   * the lane groups, then the 4 waves, are combined through LDS; a sequence that fits one
-//     partition gets its output row directly, longer ones leave (max, sum, accumulator)
-//     partials that a second kernel merges in partition order (deterministic split-K).
-// Every loop bound is uniform; loads of a step are issued together before any use so each
-// wave keeps 8 x 16-byte vectors (8 KiB per wave) in flight.
+//   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
+//     LDS with their maxima; a sequence that fits one partition gets its output row
+//     directly, longer ones leave (max, sum, accumulator) partials that a second kernel
+//     merges (deterministic split-K, no atomics).
+// Tokens past the sequence end, and blocks whose table entry lies outside the pool, are
+// excluded by selects and branches, never by multiplying by zero (the slots may hold NaN).
+// The arithmetic order does not depend on where blocks sit in the pool.
 #include <math.h>
 
 #include "common.h"
@@ -49,9 +60,18 @@ struct Cfg {
   static constexpr int TV = 64 / LV;
   static constexpr int UV = NLV >= 8 ? 1 : 8 / NLV;
   static constexpr int ACC = NLV * PER16;              // accumulators per lane per head
+  static constexpr int STEP = TK > TV ? TK : TV;       // a wave's share is a multiple of this
   static_assert(C >= 8 && C % LK == 0 && C % LV == 0, "row must be a multiple of 128 bytes");
   static_assert(TK <= 8 && TV <= 8, "a wave step must stay inside one block of >= 8 tokens");
+  static_assert(ACC * G <= 64, "accumulators per lane");
 };
+
+// Up to 256 block ids per partition, one per lane in 4 registers; j is wave-uniform.
+__device__ __forceinline__ int pick_id(const int (&ids)[4], int j) {
+  const int sel = j >> 6;
+  const int v = sel == 0 ? ids[0] : sel == 1 ? ids[1] : sel == 2 ? ids[2] : ids[3];
+  return __builtin_amdgcn_readlane(v, j & 63);
+}
 
 template <int N> __device__ __forceinline__ void lds_store_n(float* dst, const float* v) {
   if constexpr (N % 4 == 0) {
@@ -68,11 +88,11 @@ template <int N> __device__ __forceinline__ void lds_load_n(const float* src, fl
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      float4 x = *reinterpret_cast<const float4*>(src + i);
+      const float4 x = *reinterpret_cast<const float4*>(src + i);
       v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
     }
   } else if constexpr (N == 2) {
-    float2 x = *reinterpret_cast<const float2*>(src);
+    const float2 x = *reinterpret_cast<const float2*>(src);
     v[0] = x.x; v[1] = x.y;
   } else {
     v[0] = src[0];
@@ -92,76 +112,92 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float y, int ou
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
   using K = Cfg<DT, D, G>;
-  constexpr int NT = kDecodeThreads, NW = kDecodeWaves;
+  constexpr int NW = kDecodeWaves;
+  constexpr int NT = kDecodeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int pi = blockIdx.z;
+  const int pi = blockIdx.y;
+  const int b = blockIdx.z;
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
   if (pi >= nparts) return;
-  const int t0 = pi * a.part;
-  const int n = min(L - t0, a.part);  // tokens of this partition (0 only when L == 0)
-
-  const int bs_mask = (1 << a.bs_log2) - 1;
-  const int32_t* __restrict__ trow = a.block_tables + (size_t)b * a.max_blocks;
-  const size_t head_bytes = ((size_t)1 << a.bs_log2) * K::RB;     // one (block, head) tile
-  const size_t block_bytes = head_bytes * a.num_kv_heads;         // one block, all heads
-  const unsigned char* kbase = (const unsigned char*)a.k_cache + kvh * head_bytes;
-  const unsigned char* vbase = (const unsigned char*)a.v_cache + kvh * head_bytes;
-
-  const int sc_floats = max(a.part * G, NW * G * D);
-  float* s_sc = reinterpret_cast<float*>(smem);                    // [part][G] scores / probs
-  u32x4* s_q = reinterpret_cast<u32x4*>(smem + (size_t)sc_floats * 4);  // [G][C]
-  float* s_red = reinterpret_cast<float*>(smem + (size_t)sc_floats * 4 + G * K::RB);  // [2][NW][G]
+  const int t0 = pi * a.part;                  // a multiple of the block size
+  const int n = max(0, min(L - t0, a.part));   // tokens of this partition
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- stage the query group in LDS (heads kvh*G .. kvh*G+G-1 are contiguous) ----
-  const unsigned char* qsrc =
-      (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * K::RB;
-  for (int i = tid; i < G * K::C; i += NT) s_q[i] = load16(qsrc + (size_t)i * 16);
-  __syncthreads();
+  // this wave's share of the partition: [c0, c0 + nw), partition-relative
+  const int share = (((n + NW - 1) / NW) + K::STEP - 1) / K::STEP * K::STEP;
+  const int c0 = min(n, wave * share);
+  const int nw = min(n - c0, share);
 
+  // LDS: per-wave scores [NW][part/NW][G], then the merge area [NW][G][D] and [NW][G] x 2
+  const int wcap = a.part / NW;
+  float* s_sc = reinterpret_cast<float*>(smem) + (size_t)wave * wcap * G;
+  float* s_acc = reinterpret_cast<float*>(smem) + (size_t)a.part * G;
+  float* s_m = s_acc + NW * G * D;
+  float* s_l = s_m + NW * G;
+
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  const size_t head_bytes = ((size_t)1 << a.bs_log2) * K::RB;   // one (block, head) tile
+  const size_t block_bytes = head_bytes * a.num_kv_heads;       // one block, all heads
+  const unsigned char* kbase = (const unsigned char*)a.k_cache + kvh * head_bytes;
+  const unsigned char* vbase = (const unsigned char*)a.v_cache + kvh * head_bytes;
+
+  // ---- block ids of the partition (one per lane) and the query slices ----
+  const int nblk = (n + bs_mask) >> a.bs_log2;
+  const int32_t* __restrict__ trow =
+      a.block_tables + (size_t)b * a.max_blocks + (t0 >> a.bs_log2);
+  int ids[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = k * 64 + lane;
+    ids[k] = j < nblk ? trow[j] : 0;
+  }
   const int kr = lane / K::LK;  // token row inside a K step
   const int kc = lane % K::LK;  // this lane's vectors: kc, kc+LK, ...
+  const unsigned char* qsrc =
+      (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * K::RB;
   u32x4 qv[G][K::NLK];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int i = 0; i < K::NLK; ++i) qv[g][i] = s_q[g * K::C + kc + i * K::LK];
+    for (int i = 0; i < K::NLK; ++i)
+      qv[g][i] = load16(qsrc + (size_t)(g * K::C + kc + i * K::LK) * 16);
 
-  // ---- K pass: scores (base-2 units) of every token of the partition -> LDS ----
+  // ---- K pass over the wave's share: scores (log2 units) -> LDS, running max ----
   float m[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = -INFINITY;
-  const int ngk = (n + K::TK - 1) / K::TK;
-  for (int g0 = wave; g0 < ngk; g0 += NW * K::UK) {
+  const int ngk = (nw + K::TK - 1) / K::TK;
+  for (int g0 = 0; g0 < ngk; g0 += K::UK) {
     u32x4 kv[K::UK][K::NLK];
     bool okb[K::UK];
 #pragma unroll
     for (int u = 0; u < K::UK; ++u) {
-      const int gi = g0 + u * NW;
+      const int gi = g0 + u;
       okb[u] = false;
       if (gi < ngk) {
-        const int tok = t0 + gi * K::TK;
-        int blk = trow[tok >> a.bs_log2];
+        const int tok = c0 + gi * K::TK;
+        const int blk = pick_id(ids, tok >> a.bs_log2);
         okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
-        blk = okb[u] ? blk : 0;  // an invalid entry reads block 0 and is masked below
-        const unsigned char* p = kbase + (size_t)blk * block_bytes +
-                                 (size_t)((tok & bs_mask) + kr) * K::RB + kc * 16;
+        const unsigned char* p = kbase + (size_t)(okb[u] ? blk : 0) * block_bytes +
+                                 (uint32_t)(((tok & bs_mask) + kr) * K::RB + kc * 16);
 #pragma unroll
         for (int i = 0; i < K::NLK; ++i) kv[u][i] = load16(p + i * K::LK * 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < K::NLK; ++i) kv[u][i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
     for (int u = 0; u < K::UK; ++u) {
-      const int gi = g0 + u * NW;
+      const int gi = g0 + u;
       if (gi < ngk) {
         float s[G];
 #pragma unroll
@@ -172,80 +208,80 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
           s[g] = group_sum<K::LK>(acc) * a.scale_log2;
         }
         const int tl = gi * K::TK + kr;
-        const bool valid = okb[u] && tl < n;
+        const bool valid = okb[u] && tl < nw;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           s[g] = valid ? s[g] : -INFINITY;
           m[g] = fmaxf(m[g], s[g]);
         }
-        if (kc == 0 && tl < n) lds_store_n<G>(s_sc + tl * G, s);
+        if (kc == 0 && tl < nw) lds_store_n<G>(s_sc + tl * G, s);
       }
     }
   }
-
-  // ---- partition max: lanes of one row agree; combine rows, then waves ----
+  // the wave's max (every lane ends with it); -inf when the share has no readable token
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = xor_max_from<K::LK>(m[g]);
-  if (lane == 0) lds_store_n<G>(s_red + wave * G, m);
-  __syncthreads();
-  float mg[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x = s_red[g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) x = fmaxf(x, s_red[w * G + g]);
-    mg[g] = x == -INFINITY ? 0.f : x;  // nothing valid: every weight becomes exp2(-inf) = 0
-  }
 
-  // ---- probabilities p = 2^(s - max) in place, and this lane's share of their sum ----
+  // ---- first round of V loads, issued before the exponentials ----
+  const int vr = lane / K::LV;
+  const int vc = lane % K::LV;
+  const int ngv = (nw + K::TV - 1) / K::TV;
+  u32x4 vv[K::UV][K::NLV];
+  bool okv[K::UV];
+  auto load_v = [&](int g0) {
+#pragma unroll
+    for (int u = 0; u < K::UV; ++u) {
+      const int gi = g0 + u;
+      okv[u] = false;
+      if (gi < ngv) {
+        const int tok = c0 + gi * K::TV;
+        const int blk = pick_id(ids, tok >> a.bs_log2);
+        okv[u] = (unsigned)blk < (unsigned)a.num_blocks;
+        const unsigned char* p = vbase + (size_t)(okv[u] ? blk : 0) * block_bytes +
+                                 (uint32_t)(((tok & bs_mask) + vr) * K::RB + vc * 16);
+#pragma unroll
+        for (int i = 0; i < K::NLV; ++i) vv[u][i] = load16(p + i * K::LV * 16);
+      }
+    }
+  };
+  load_v(0);
+
+  // ---- probabilities 2^(s - max) in place, once per (token, head); their sum ----
   float l[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) l[g] = 0.f;
-  for (int t = tid; t < n; t += NT) {
+  __builtin_amdgcn_wave_barrier();
+  float mz[G];  // exponent base: the max, or 0 when nothing is readable (then every p is 0)
+#pragma unroll
+  for (int g = 0; g < G; ++g) mz[g] = m[g] == -INFINITY ? 0.f : m[g];
+  for (int t = lane; t < nw; t += 64) {
     float v[G];
     lds_load_n<G>(s_sc + t * G, v);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      v[g] = exp2f(v[g] - mg[g]);
+      v[g] = exp2f(v[g] - mz[g]);  // a stored -inf gives 0
       l[g] += v[g];
     }
     lds_store_n<G>(s_sc + t * G, v);
   }
-  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) l[g] = xor_sum_from<1>(l[g]);
+  __builtin_amdgcn_wave_barrier();
 
-  // ---- V pass: acc[g][:] += p[g] * v over the partition ----
-  const int vr = lane / K::LV;
-  const int vc = lane % K::LV;
+  // ---- V pass: acc[g][:] += p[g] * v over the wave's share ----
   float acc[G][K::ACC];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < K::ACC; ++e) acc[g][e] = 0.f;
-  const int ngv = (n + K::TV - 1) / K::TV;
-  for (int g0 = wave; g0 < ngv; g0 += NW * K::UV) {
-    u32x4 vv[K::UV][K::NLV];
-    bool okb[K::UV];
+  for (int g0 = 0; g0 < ngv; g0 += K::UV) {
+    if (g0 > 0) load_v(g0);
 #pragma unroll
     for (int u = 0; u < K::UV; ++u) {
-      const int gi = g0 + u * NW;
-      okb[u] = false;
-      if (gi < ngv) {
-        const int tok = t0 + gi * K::TV;
-        int blk = trow[tok >> a.bs_log2];
-        okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
-        blk = okb[u] ? blk : 0;
-        const unsigned char* p = vbase + (size_t)blk * block_bytes +
-                                 (size_t)((tok & bs_mask) + vr) * K::RB + vc * 16;
-#pragma unroll
-        for (int i = 0; i < K::NLV; ++i) vv[u][i] = load16(p + i * K::LV * 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < K::UV; ++u) {
-      const int gi = g0 + u * NW;
+      const int gi = g0 + u;
       const int tl = gi * K::TV + vr;
       // tokens past the sequence end may hold anything (even NaN): skip, never multiply by 0
-      if (gi < ngv && okb[u] && tl < n) {
+      if (gi < ngv && okv[u] && tl < nw) {
         float pg[G];
         lds_load_n<G>(s_sc + tl * G, pg);
 #pragma unroll
@@ -262,15 +298,11 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
   }
 
-  // ---- combine: rows inside each wave (shuffles), then the waves (LDS) ----
+  // ---- the wave's rows summed; the wave's (max, sum, accumulator) -> LDS ----
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < K::ACC; ++e) acc[g][e] = xor_sum_from<K::LV>(acc[g][e]);
-    l[g] = xor_sum_from<1>(l[g]);
-  }
-  __syncthreads();  // every wave is done reading probabilities from s_sc
-  float* s_acc = s_sc;  // [NW][G][D]
   if (vr == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -279,76 +311,121 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         lds_store_n<K::PER16>(s_acc + (wave * G + g) * D + (i * K::LV + vc) * K::PER16,
                               &acc[g][i * K::PER16]);
   }
-  if (lane == 0) lds_store_n<G>(s_red + NW * G + wave * G, l);
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s_m[wave * G + g] = m[g];
+      s_l[wave * G + g] = l[g];
+    }
+  }
   __syncthreads();
 
+  // ---- merge the waves; write the output row or this partition's partials ----
   const bool single = nparts == 1;
   for (int idx = tid; idx < G * D; idx += NT) {
     const int g = idx / D;
     const int d = idx - g * D;
-    float x = s_acc[g * D + d];
-    float lt = s_red[NW * G + g];
+    float M = s_m[g];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      x += s_acc[(w * G + g) * D + d];
-      lt += s_red[NW * G + w * G + g];
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w * G + g]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = s_m[w * G + g];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      num = __builtin_fmaf(f, s_acc[(w * G + g) * D + d], num);
+      den = __builtin_fmaf(f, s_l[w * G + g], den);
     }
     const int h = kvh * G + g;
     if (single) {
-      const float y = lt > 0.f ? x / lt : 0.f;
+      const float y = den > 0.f ? num / den : 0.f;
       store_out(a.out, ((size_t)b * a.num_q_heads + h) * D + d, y, a.out_dtype);
     } else {
       const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + pi;
-      a.ws_acc[slot * D + d] = x;
+      a.ws_acc[slot * D + d] = num;
       if (d == 0) {
-        float mm = s_red[g];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) mm = fmaxf(mm, s_red[w * G + g]);
-        a.ws_ml[slot * 2] = mm == -INFINITY ? 0.f : mm;
-        a.ws_ml[slot * 2 + 1] = lt;
+        a.ws_ml[slot * 2] = M;  // -inf when the partition had no readable token
+        a.ws_ml[slot * 2 + 1] = den;
       }
     }
   }
 }
 
-// Merge of the partitions of one (sequence, query head), in partition order:
+// Merge of the partitions of one (sequence, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p.
+// 256 lanes: D/4 lanes cover a row with 16-byte loads and 1024/D slices take the partitions
+// in turn (slice s gets p = s, s + S, ...); the slices are combined in slice order, so the
+// result is deterministic.
 template <int D>
-__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 4;          // lanes per row
+  constexpr int S = 256 / LPR;        // partition slices
+  __shared__ float s_max[S];
+  __shared__ float4 s_num[S][LPR];
+  __shared__ float s_den[S];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
   if (nparts <= 1) return;
+  const int sl = threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
   const size_t base = ((size_t)b * a.num_q_heads + h) * a.pmax;
   const float* __restrict__ ml = a.ws_ml + base * 2;
-  const float* __restrict__ acc = a.ws_acc + base * D + d;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = exp2f(ml[2 * p] - M);
+  const float4* __restrict__ acc = reinterpret_cast<const float4*>(a.ws_acc + base * D) + c;
+
+  float mx = -INFINITY;
+  for (int p = sl; p < nparts; p += S) mx = fmaxf(mx, ml[2 * p]);
+  if (c == 0) s_max[sl] = mx;
+  __syncthreads();
+  float M = s_max[0];
+#pragma unroll
+  for (int i = 1; i < S; ++i) M = fmaxf(M, s_max[i]);
+
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int p = sl; p < nparts; p += S) {
+    const float mp = ml[2 * p];
+    const float w = mp == -INFINITY ? 0.f : exp2f(mp - M);
+    const float4 x = acc[(size_t)p * LPR];
     den = __builtin_fmaf(w, ml[2 * p + 1], den);
-    num = __builtin_fmaf(w, acc[(size_t)p * D], num);
+    num.x = __builtin_fmaf(w, x.x, num.x);
+    num.y = __builtin_fmaf(w, x.y, num.y);
+    num.z = __builtin_fmaf(w, x.z, num.z);
+    num.w = __builtin_fmaf(w, x.w, num.w);
   }
-  const float y = den > 0.f ? num / den : 0.f;
-  store_out(a.out, ((size_t)b * a.num_q_heads + h) * D + d, y, a.out_dtype);
+  s_num[sl][c] = num;
+  if (c == 0) s_den[sl] = den;
+  __syncthreads();
+  if (sl == 0) {
+    float4 t = s_num[0][c];
+    float dt = s_den[0];
+#pragma unroll
+    for (int i = 1; i < S; ++i) {
+      const float4 x = s_num[i][c];
+      t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+      dt += s_den[i];
+    }
+    const size_t o = ((size_t)b * a.num_q_heads + h) * D + c * 4;
+    const bool ok = dt > 0.f;
+    store_out(a.out, o + 0, ok ? t.x / dt : 0.f, a.out_dtype);
+    store_out(a.out, o + 1, ok ? t.y / dt : 0.f, a.out_dtype);
+    store_out(a.out, o + 2, ok ? t.z / dt : 0.f, a.out_dtype);
+    store_out(a.out, o + 3, ok ? t.w / dt : 0.f, a.out_dtype);
+  }
 }
 
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
-  const int eb = kv_dtype == F32 ? 4 : 2;
-  const size_t sc = (size_t)(part * group > kDecodeWaves * group * head_dim
-                                 ? part * group
-                                 : kDecodeWaves * group * head_dim);
-  return sc * 4 + (size_t)group * head_dim * eb + 2 * kDecodeWaves * group * 4;
+  (void)kv_dtype;
+  // per-wave scores (part x group floats in all) + merge area
+  return ((size_t)part * group + (size_t)kDecodeWaves * group * (head_dim + 2)) * 4;
 }
 
 template <int DT, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_kv_heads, a.num_seqs, a.pmax);
+  const dim3 grid(a.num_kv_heads, a.pmax, a.num_seqs);
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
   hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G>), grid, dim3(kDecodeThreads), lds,
                      stream, a);
@@ -391,8 +468,8 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.num_seqs);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(paged_decode_reduce_kernel<64>, grid, dim3(64), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(paged_decode_reduce_kernel<128>, grid, dim3(128), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(paged_decode_reduce_kernel<64>, grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(paged_decode_reduce_kernel<128>, grid, dim3(256), 0, stream, a); break;
     case 256: hipLaunchKernelGGL(paged_decode_reduce_kernel<256>, grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
