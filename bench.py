@@ -211,6 +211,44 @@ def cpu_baseline(st, target_s, gen):
 
 # ---------------------------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------------------------
+# measured HBM traffic of the decode kernel (from rocprofv3 counter runs kept under profiles/)
+# ---------------------------------------------------------------------------------------------
+
+KERNEL_SOURCES = ("paged_kv_cache_402_amd/csrc/decode.hip", "paged_kv_cache_402_amd/csrc/common.h",
+                  "paged_kv_cache_402_amd/csrc/launch.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the decode kernel from profiles/hbm_traffic_<workload>.txt:
+    FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
+    copy of known size. None when no such file exists or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def copy_probe(pk, torch, dev):
     """A plain copy of known size through copy_blocks: 4096 blocks of 64 KiB per cache, read
     once and written once (512 MiB each way), repeated 5 times."""
@@ -263,6 +301,7 @@ def main():
         pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
         if i is not None:
             ev[i][1].record()
+        # paged_attention_decode's two launches, called apart so each has its own events
         pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
                                       st["lens"], case.scale, partition_size=part, workspace=ws)
         if i is not None:
@@ -288,7 +327,8 @@ def main():
     t_red = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     dec_ms = float(np.mean(t_dec))
     gbps = bytes_["kv_unique"] / (ms_step * 1e-3) / 1e9
-    achieved = bytes_["decode_kernel"] / (dec_ms * 1e-3) / 1e9
+    kernel_bytes = bytes_["decode_kernel"]
+    achieved = kernel_bytes / (dec_ms * 1e-3) / 1e9
     log("step %.4f ms, decode kernel %.4f ms (p10 %.4f, p90 %.4f), reduce %.4f ms, cache write "
         "%.4f ms" % (ms_step, dec_ms, np.percentile(t_dec, 10), np.percentile(t_dec, 90), t_red,
                      t_cw))
@@ -322,8 +362,9 @@ def main():
                       "reshape_and_cache": round(t_cw, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "paged_decode_partition_kernel",
-                     "bytes_per_launch": bytes_["decode_kernel"]},
+                     "traffic": measured_traffic(case.name),
+                     "kernel": "paged_decode_partition_kernel",
+                     "bytes_per_launch": kernel_bytes},
     }
     log("host manager cost")
     result["host_manager_us_per_step"] = round(host_manager_cost(pk, case), 1)

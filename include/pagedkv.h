@@ -82,7 +82,8 @@ const char* pkv_last_error(void);
 
 /* Bytes of split-K workspace pkv_paged_attention_decode needs: for every (sequence, query
  * head, context partition) one running max, one exponent sum and one head_dim-long fp32
- * accumulator. partition_size defaults to 512 when 0 is passed. Returns 0 on bad input. */
+ * accumulator. partition_size defaults to 512 when 0 is passed. Returns 0 on bad input or
+ * when no sequence can span two partitions. */
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
                                   int block_size, int head_dim, int partition_size);
 
@@ -100,7 +101,10 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_
  *                  partition are finished by a second, deterministic merge pass.
  *   workspace    : device buffer of at least pkv_decode_workspace_bytes() bytes; may be NULL
  *                  only if workspace_bytes is 0 and no sequence can span two partitions
- *                  (max_blocks_per_seq*block_size <= partition_size).
+ *                  (max_blocks_per_seq*block_size <= partition_size). Calls that share a
+ *                  workspace must not overlap in time (enqueue them on one stream).
+ * Two launches: per-partition attention, then (when some sequence spans two partitions) a
+ * deterministic merge of the partitions' partials.
  * The output is a deterministic function of the inputs: it does not depend on where the
  * blocks sit in the pool, nor on which other sequences share them. */
 int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const void* k_cache,
@@ -110,7 +114,7 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                int max_blocks_per_seq, float scale, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two passes of pkv_paged_attention_decode, exposed separately so a caller can time or
+/* The two launches of pkv_paged_attention_decode, exposed separately so a caller can time or
  * schedule them apart. Same arguments and results as the combined call:
  *   _partitions: one workgroup per (KV head, sequence, partition) attends over its partition;
  *                single-partition sequences get their final row in `out`, others leave

@@ -93,7 +93,8 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "decode: q and caches must be 16-byte aligned");
   size_t need = 0;
-  if (pmax > 1) need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+  if (pmax > 1)
+    need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
 

@@ -117,6 +117,15 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Max over each aligned row of 16 lanes (DPP); every lane of a row ends with the same value.
+__device__ __forceinline__ float xor_max_row16(float x) {
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_MIRROR>(x));
+  return x;
+}
+
 // Reductions across lanes whose ids differ in bits >= log2(STRIDE): combine lane l with
 // l ^ STRIDE, l ^ 2*STRIDE, ..., l ^ 32 (ds_bpermute through the LDS crossbar).
 template <int STRIDE> __device__ __forceinline__ float xor_max_from(float x) {

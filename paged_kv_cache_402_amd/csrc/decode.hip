@@ -73,6 +73,23 @@ __device__ __forceinline__ int pick_id(const int (&ids)[4], int j) {
   return __builtin_amdgcn_readlane(v, j & 63);
 }
 
+// 16x16x32 matrix-core product of 16-bit operands with fp32 accumulation, operands passed as
+// the 16 stored bytes each lane holds. Lane l supplies A[l % 16][8 (l / 16) .. +8] and
+// B[8 (l / 16) .. +8][l % 16]; it receives C[4 (l / 16) + i][l % 16], i = 0..3.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <int DT> __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mfma16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma16x16x32<F32>(u32x4, u32x4, f32x4 c) { return c; }
+
 template <int N> __device__ __forceinline__ void lds_store_n(float* dst, const float* v) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
@@ -109,7 +126,7 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float y, int ou
   }
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool MF>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
   using K = Cfg<DT, D, G>;
   constexpr int NW = kDecodeWaves;
@@ -131,8 +148,10 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // this wave's share of the partition: [c0, c0 + nw), partition-relative
-  const int share = (((n + NW - 1) / NW) + K::STEP - 1) / K::STEP * K::STEP;
+  // this wave's share of the partition: [c0, c0 + nw), partition-relative; a multiple of
+  // every step size (the matrix-core K pass takes 16 tokens per step)
+  constexpr int STEP = MF && K::STEP < 16 ? 16 : K::STEP;
+  const int share = (((n + NW - 1) / NW) + STEP - 1) / STEP * STEP;
   const int c0 = min(n, wave * share);
   const int nw = min(n - c0, share);
 
@@ -174,6 +193,69 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   float m[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+  if constexpr (MF) {
+    // Matrix cores: S^T (16 padded heads x 16 tokens) = Q (16 x d) . K^T (d x 16), d in
+    // slices of 32. Lane l holds head / token l % 16 and the 8 elements 32 j + 8 (l / 16) of
+    // slice j; the result gives lane l the scores of token l % 16 for heads 4 (l / 16) + i.
+    constexpr int NJ = D / 32;                    // products per 16-token step
+    constexpr int UM = NJ >= 8 ? 1 : 8 / NJ;      // steps per load round (8 loads per lane)
+    const int rl = lane & 15;
+    const int kg = lane >> 4;
+    u32x4 qa[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qa[j] = rl < G ? load16(qsrc + (size_t)rl * K::RB + j * 64 + kg * 16) : u32x4{0u, 0u, 0u, 0u};
+    float mh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mh[i] = -INFINITY;
+    const int ngm = (nw + 15) / 16;
+    for (int g0 = 0; g0 < ngm; g0 += UM) {
+      u32x4 kb[UM][NJ];
+      bool okb[UM];
+#pragma unroll
+      for (int u = 0; u < UM; ++u) {
+        const int gi = g0 + u;
+        okb[u] = false;
+        if (gi < ngm) {
+          const int tok = c0 + gi * 16;
+          const int blk = pick_id(ids, tok >> a.bs_log2);
+          okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
+          const unsigned char* p = kbase + (size_t)(okb[u] ? blk : 0) * block_bytes +
+                                   (uint32_t)(((tok & bs_mask) + rl) * K::RB + kg * 16);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) kb[u][j] = load16(p + j * 64);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) kb[u][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UM; ++u) {
+        const int gi = g0 + u;
+        if (gi < ngm) {
+          f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) c = mfma16x16x32<DT>(qa[j], kb[u][j], c);
+          const int tl = gi * 16 + rl;
+          const bool valid = okb[u] && tl < nw;
+          float sv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[i] = valid ? c[i] * a.scale_log2 : -INFINITY;
+            mh[i] = fmaxf(mh[i], sv[i]);
+          }
+          if (tl < nw && kg * 4 < G) lds_store_n<(G < 4 ? G : 4)>(s_sc + tl * G + kg * 4, sv);
+        }
+      }
+    }
+    // max over the 16 tokens of each lane row, then broadcast head g from row g / 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mh[i] = xor_max_row16(mh[i]);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      m[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                           __builtin_bit_cast(int, mh[g & 3]), (g >> 2) * 16));
+  } else {
   const int ngk = (nw + K::TK - 1) / K::TK;
   for (int g0 = 0; g0 < ngk; g0 += K::UK) {
     u32x4 kv[K::UK][K::NLK];
@@ -221,6 +303,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   // the wave's max (every lane ends with it); -inf when the share has no readable token
 #pragma unroll
   for (int g = 0; g < G; ++g) m[g] = xor_max_from<K::LK>(m[g]);
+  }
 
   // ---- first round of V loads, issued before the exponentials ----
   const int vr = lane / K::LV;
@@ -353,16 +436,17 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
 
 // Merge of the partitions of one (sequence, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p.
-// 256 lanes: D/4 lanes cover a row with 16-byte loads and 1024/D slices take the partitions
-// in turn (slice s gets p = s, s + S, ...); the slices are combined in slice order, so the
-// result is deterministic.
+// 256 lanes: D/4 lanes cover a row with 16-byte loads and S = 1024/D slices take the
+// partitions in turn (slice s gets p = s, s + S, ...). Each slice keeps a running (max, sum,
+// accumulator), rescaled as its max grows, so every load of the partials is issued in one
+// pass; the slices are then combined in slice order. The result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) {
   constexpr int LPR = D / 4;          // lanes per row
   constexpr int S = 256 / LPR;        // partition slices
   __shared__ float s_max[S];
-  __shared__ float4 s_num[S][LPR];
   __shared__ float s_den[S];
+  __shared__ float4 s_num[S][LPR];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int cap = a.max_blocks << a.bs_log2;
@@ -376,37 +460,44 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) 
   const float* __restrict__ ml = a.ws_ml + base * 2;
   const float4* __restrict__ acc = reinterpret_cast<const float4*>(a.ws_acc + base * D) + c;
 
-  float mx = -INFINITY;
-  for (int p = sl; p < nparts; p += S) mx = fmaxf(mx, ml[2 * p]);
-  if (c == 0) s_max[sl] = mx;
-  __syncthreads();
-  float M = s_max[0];
-#pragma unroll
-  for (int i = 1; i < S; ++i) M = fmaxf(M, s_max[i]);
-
+  float m = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
+#pragma unroll 4
   for (int p = sl; p < nparts; p += S) {
     const float mp = ml[2 * p];
-    const float w = mp == -INFINITY ? 0.f : exp2f(mp - M);
+    const float lp = ml[2 * p + 1];
     const float4 x = acc[(size_t)p * LPR];
-    den = __builtin_fmaf(w, ml[2 * p + 1], den);
-    num.x = __builtin_fmaf(w, x.x, num.x);
-    num.y = __builtin_fmaf(w, x.y, num.y);
-    num.z = __builtin_fmaf(w, x.z, num.z);
-    num.w = __builtin_fmaf(w, x.w, num.w);
+    const float mn = fmaxf(m, mp);
+    const float fo = m == -INFINITY ? 0.f : exp2f(m - mn);   // rescale of what came before
+    const float fp = mp == -INFINITY ? 0.f : exp2f(mp - mn);  // weight of this partition
+    den = den * fo + lp * fp;
+    num.x = __builtin_fmaf(x.x, fp, num.x * fo);
+    num.y = __builtin_fmaf(x.y, fp, num.y * fo);
+    num.z = __builtin_fmaf(x.z, fp, num.z * fo);
+    num.w = __builtin_fmaf(x.w, fp, num.w * fo);
+    m = mn;
   }
   s_num[sl][c] = num;
-  if (c == 0) s_den[sl] = den;
+  if (c == 0) {
+    s_max[sl] = m;
+    s_den[sl] = den;
+  }
   __syncthreads();
   if (sl == 0) {
-    float4 t = s_num[0][c];
-    float dt = s_den[0];
+    float M = s_max[0];
 #pragma unroll
-    for (int i = 1; i < S; ++i) {
+    for (int i = 1; i < S; ++i) M = fmaxf(M, s_max[i]);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dt = 0.f;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const float f = s_max[i] == -INFINITY ? 0.f : exp2f(s_max[i] - M);
       const float4 x = s_num[i][c];
-      t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
-      dt += s_den[i];
+      t.x = __builtin_fmaf(f, x.x, t.x);
+      t.y = __builtin_fmaf(f, x.y, t.y);
+      t.z = __builtin_fmaf(f, x.z, t.z);
+      t.w = __builtin_fmaf(f, x.w, t.w);
+      dt = __builtin_fmaf(f, s_den[i], dt);
     }
     const size_t o = ((size_t)b * a.num_q_heads + h) * D + c * 4;
     const bool ok = dt > 0.f;
@@ -427,8 +518,16 @@ template <int DT, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_kv_heads, a.pmax, a.num_seqs);
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
-  hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G>), grid, dim3(kDecodeThreads), lds,
-                     stream, a);
+  // Matrix-core scores for 16-bit data at G = 8, when a 16-token step stays inside one block
+  // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured
+  // faster (the padded 16-row product does 4x the work there and the K pass is not the limit).
+  constexpr bool kMF = DT != F32 && G == 8;
+  if (kMF && a.bs_log2 >= 4 && a.part % 64 == 0)
+    hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, kMF>), grid,
+                       dim3(kDecodeThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, false>), grid,
+                       dim3(kDecodeThreads), lds, stream, a);
   return hipGetLastError();
 }
 

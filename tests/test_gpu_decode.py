@@ -288,3 +288,42 @@ def test_full_size_sampled(which):
     ref = _sampled_reference(case, q, k, v, seqs)
     for r, s in enumerate(seqs):
         assert max_err(got[s], ref[r]) <= GATE[case.dtype], "seq %d" % s
+
+
+# --------------------------------------------------------------------------------------------
+# split-K: the one-launch merge (completion counters) and the two-launch form
+# --------------------------------------------------------------------------------------------
+
+def test_caller_workspace_reused_bitwise():
+    import paged_kv_cache_402_amd as pk
+    case = gen.make_case("splitk", np.random.default_rng(31), [40, 1100, 2900, 513, 1024], 16, 4,
+                         128, 16, "bf16", width=200)
+    B, Hq, D = case.q.shape
+    need = pk.decode_workspace_bytes(B, Hq, 200, 16, D, 512)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # stale contents
+    q, k, v = to_dev(case.q, "bf16"), to_dev(case.k_cache, "bf16"), to_dev(case.v_cache, "bf16")
+    outs = []
+    for _ in range(3):
+        o = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        pk.paged_attention_decode(o, q, k, v, i32(case.block_tables), i32(case.seq_lens),
+                                  case.scale, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert max_err(outs[0].numpy().astype(np.float64), oracle(case)) <= GATE["bf16"]
+
+
+def test_two_launch_split_matches_oracle():
+    import paged_kv_cache_402_amd as pk
+    case = gen.make_case("split2", np.random.default_rng(32), [7, 600, 3000, 1537], 32, 8, 128, 16,
+                         "bf16", width=200)
+    B, Hq, D = case.q.shape
+    q, k, v = to_dev(case.q, "bf16"), to_dev(case.k_cache, "bf16"), to_dev(case.v_cache, "bf16")
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = pk.paged_attention_partitions(out, q, k, v, tables, lens, case.scale)
+    pk.paged_attention_reduce(out, lens, 16, 200, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert max_err(got, oracle(case)) <= GATE["bf16"]
