@@ -35,7 +35,8 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
-BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk")
+BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk",
+                   "llama13b_longtail")
 
 
 def parse_args():
@@ -61,7 +62,49 @@ def log(msg):
 # workload set-up through the block manager
 # ---------------------------------------------------------------------------------------------
 
+def build_forked_state(pk, gen, torch, dev):
+    """Parallel sampling step: every prompt is forked into its branches, then each branch
+    appends one token; branches whose last prompt block is partial copy it first (the manager
+    emits the copy-on-write pairs). The timed step replays that step: copy_blocks of the same
+    pairs, cache write of the same slots, decode over the same tables."""
+    fc = gen.llama13b_longtail_case(values=False)
+    bs, nb = fc.block_size, fc.num_blocks
+    bm = pk.BlockManager(nb, bs, fc.free_order)
+    for g, L in enumerate(fc.decode_lens.tolist()):
+        parent = g * fc.branches
+        bm.add_seq(parent, L - 1)
+        for br in range(1, fc.branches):
+            bm.fork(parent, parent + br)
+    B = fc.num_seqs
+    slots, pairs = bm.append_slots(range(B))
+    tables, seq_lens = bm.build_tables(range(B), fc.table_width)
+    case = gen.PagedDecodeCase(fc.name, fc.dtype, fc.num_q_heads, fc.num_kv_heads, fc.head_dim, bs,
+                               nb, seq_lens, tables, fc.scale,
+                               meta={"cow_pairs": int(pairs.shape[0]), "branches": fc.branches})
+    return case, bm, slots, pairs
+
+
 def build_state(name, pk, gen, torch, dev):
+    if name == "llama13b_longtail":
+        case, bm, slots, pairs = build_forked_state(pk, gen, torch, dev)
+        B = case.num_seqs
+        shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+        seed = 402100
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+        return {
+            "case": case, "bm": bm,
+            "k": gen.device_normal(shape, case.dtype, seed, dev),
+            "v": gen.device_normal(shape, case.dtype, seed + 1, dev),
+            "q": gen.device_normal((B, case.num_q_heads, case.head_dim), case.dtype, seed + 2, dev),
+            "k_new": gen.device_normal((B, case.num_kv_heads, case.head_dim), case.dtype, seed + 3, dev),
+            "v_new": gen.device_normal((B, case.num_kv_heads, case.head_dim), case.dtype, seed + 4, dev),
+            "tables": torch.from_numpy(case.block_tables).to(dev),
+            "lens": torch.from_numpy(case.seq_lens).to(dev),
+            "slots": torch.from_numpy(slots).to(dev),
+            "pairs": torch.from_numpy(np.ascontiguousarray(pairs.reshape(-1, 2))).to(dev)
+            if pairs.shape[0] else None,
+            "out": torch.empty((B, case.num_q_heads, case.head_dim), dtype=tdt, device=dev),
+        }
     maker = gen.WORKLOADS[name]
     case = maker(values=False)
     B, bs, W = case.num_seqs, case.block_size, case.table_width
@@ -116,7 +159,8 @@ def host_manager_cost(pk, case, iters=20):
     B, bs = case.num_seqs, case.block_size
     lens = case.seq_lens.astype(np.int64)
     width = case.table_width + iters // bs + 2
-    bm = pk.BlockManager(case.num_blocks + B * (iters // bs + 2), bs)
+    need = int((-(-lens // bs)).sum())
+    bm = pk.BlockManager(max(case.num_blocks, need) + B * (iters // bs + 2), bs)
     prefix = case.meta.get("prefix_tokens", 0)
     if prefix:
         bm.add_seq(-1, prefix)
@@ -291,9 +335,11 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
 
     def step(i=None):
+        if i is not None:
+            ev[i][4].record()
         if st["pairs"] is not None:
             pk.copy_blocks(st["k"], st["v"], st["pairs"])
         if i is not None:
@@ -323,6 +369,7 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
     t_cw = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_cb = float(np.mean([e[4].elapsed_time(e[0]) for e in ev]))
     t_dec = [e[1].elapsed_time(e[2]) for e in ev]
     t_red = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     dec_ms = float(np.mean(t_dec))
@@ -359,6 +406,7 @@ def main():
         "kv_logical_bytes": bytes_["kv_logical"],
         "effective_logical_GBps": round(bytes_["kv_logical"] / (ms_step * 1e-3) / 1e9, 2),
         "kernel_ms": {"decode_partitions": round(dec_ms, 5), "partition_reduce": round(t_red, 5),
+                      "copy_blocks": round(t_cb, 5) if st["pairs"] is not None else None,
                       "reshape_and_cache": round(t_cw, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -212,11 +212,35 @@ int pkv_bm_build_tables(const pkv_bm* bm, const int64_t* seqs, int n, int32_t* t
 /* Refcount of one block (0 = free), or <0 for an id outside the pool. */
 int pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 
-/* Counters for pool monitoring (P3 §2.2.13 asks for pool occupancy and allocation
- * failures): out[0] blocks in use, [1] free blocks, [2] shared blocks (refcount > 1),
- * [3] copy-on-write copies issued, [4] allocation failures, [5] live sequences,
- * [6] reserved (0), [7] reserved (0). */
+/* Counters for pool monitoring (P3 §2.2.13 asks for pool occupancy, allocation failures and
+ * the prefix-cache hit rate): out[0] blocks held by sequences, [1] blocks available for
+ * allocation (free, plus cached blocks no sequence holds), [2] shared blocks (refcount > 1),
+ * [3] copy-on-write copies issued, [4] allocation failures, [5] live sequences, [6] prefix
+ * cache hits (blocks reused by pkv_bm_add_seq_cached), [7] prefix cache lookups (full prompt
+ * blocks looked up). */
 int pkv_bm_stats(const pkv_bm* bm, int64_t out[8]);
+
+/* ------------------------------------------------------------------------------------------
+ * Prefix caching (P1 §7.4; P3 §2.2.8, §2.2.13): requests that start with the same tokens
+ * (a shared system prompt) reuse the physical blocks that already hold those tokens' K/V.
+ * Only full blocks of prompts added with pkv_bm_add_seq_cached are cached. A block is
+ * registered under its key: the block before it (its id and how many times it has been
+ * handed out, or none) and its block_size token ids, so a key names the whole token prefix
+ * up to that block exactly; there are no hash collisions. Cached blocks that no sequence
+ * holds any more stay cached and count as available; they are handed out again only when no
+ * free block is left, the one released longest ago first, and then leave the cache.
+ * ------------------------------------------------------------------------------------------ */
+
+/* New sequence holding the num_tokens prompt tokens token_ids[0..num_tokens). Its leading
+ * full blocks whose token prefix is cached are reused (refcount + 1); the rest are fresh
+ * blocks, and the fresh full ones are registered. *num_cached_tokens (may be NULL) receives
+ * how many leading tokens are already in the cache: the caller writes K/V only for the
+ * tokens after them (slots from pkv_bm_slots). Fails atomically with PKV_ENOBLOCKS. */
+int pkv_bm_add_seq_cached(pkv_bm* bm, int64_t seq, const int32_t* token_ids, int num_tokens,
+                          int* num_cached_tokens);
+
+/* out[0] registered blocks, [1] of them held by no sequence, [2] hits, [3] lookups. */
+int pkv_bm_prefix_stats(const pkv_bm* bm, int64_t out[4]);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ Readings where the pages are silent or garbled (listed in the design doc):
     opens a new block at token index 48. The model follows the arithmetic.
 """
 
+import copy
+
 OK = 0
 EINVAL = -1
 ENOBLOCKS = -3
@@ -42,6 +44,56 @@ class BlockManagerModel:
         self.seqs = {}                           # seq -> [blocks, num_tokens]
         self.cow_copies = 0
         self.alloc_failures = 0
+        # prefix cache (P1 §7.4; P3 §2.2.8): key -> block for full prompt blocks; a key is
+        # (previous block, its hand-out count, the block's tokens), so it names the exact
+        # token prefix; unheld cached blocks wait in release order and are reused last
+        self.cache = {}
+        self.block_key = {}
+        self.released = []                       # cached blocks no sequence holds, oldest first
+        self.handouts = [0] * num_blocks
+        self.prefix_hits = 0
+        self.prefix_lookups = 0
+        self.prefix_tokens = {}                  # block -> the full token prefix it ends
+
+    # -- all-or-nothing support for multi-step operations ------------------------------------
+    def snapshot(self):
+        keep = self.alloc_failures
+        state = copy.deepcopy({k: v for k, v in self.__dict__.items() if k != "alloc_failures"})
+        return state, keep
+
+    def restore(self, snap):
+        state, _ = snap
+        failures = self.alloc_failures
+        self.__dict__.update(copy.deepcopy(state))
+        self.alloc_failures = failures
+
+    # -- block hand-out and release -------------------------------------------------------------
+    def _available(self):
+        return len(self.free) + len(self.released)
+
+    def _take(self):
+        if self.free:
+            b = self.free.pop()
+        else:                                    # oldest released cached block leaves the cache
+            b = self.released.pop(0)
+            del self.cache[self.block_key.pop(b)]
+            self.prefix_tokens.pop(b, None)
+        self.rc[b] = 1
+        self.handouts[b] += 1
+        return b
+
+    def _hold(self, b):
+        if self.rc[b] == 0 and b in self.released:
+            self.released.remove(b)
+        self.rc[b] += 1
+
+    def _release(self, b):
+        self.rc[b] -= 1
+        if self.rc[b] == 0:
+            if b in self.block_key:
+                self.released.append(b)
+            else:
+                self.free.append(b)
 
     def _need(self, n):
         return (n + self.block_size - 1) // self.block_size
@@ -50,14 +102,52 @@ class BlockManagerModel:
         if seq in self.seqs or num_tokens < 0:
             return EINVAL
         need = self._need(num_tokens)
-        if need > len(self.free):
+        if need > self._available():
             self.alloc_failures += 1
             return ENOBLOCKS
-        blocks = [self.free.pop() for _ in range(need)]
-        for b in blocks:
-            self.rc[b] = 1
+        blocks = [self._take() for _ in range(need)]
         self.seqs[seq] = [blocks, num_tokens]
         return OK
+
+    def _key(self, parent, tokens):
+        return (parent, self.handouts[parent] if parent >= 0 else 0, tuple(int(t) for t in tokens))
+
+    def add_seq_cached(self, seq, token_ids):
+        """Returns (status, cached tokens): leading full blocks whose exact token prefix is
+        cached are reused, the rest are fresh and the fresh full blocks get registered."""
+        tokens = [int(t) for t in token_ids]
+        if seq in self.seqs:
+            return EINVAL, 0
+        bs = self.block_size
+        nfull = len(tokens) // bs
+        hits, parent = [], -1
+        for j in range(nfull):
+            b = self.cache.get(self._key(parent, tokens[j * bs:(j + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+            parent = b
+        need = self._need(len(tokens)) - len(hits)
+        unheld_hits = sum(1 for b in hits if self.rc[b] == 0)
+        if need > self._available() - unheld_hits:
+            self.alloc_failures += 1
+            return ENOBLOCKS, 0
+        for b in hits:
+            self._hold(b)
+        blocks = list(hits)
+        for j in range(len(hits), self._need(len(tokens))):
+            b = self._take()
+            blocks.append(b)
+            if j < nfull:
+                key = self._key(parent, tokens[j * bs:(j + 1) * bs])
+                self.cache[key] = b
+                self.block_key[b] = key
+                self.prefix_tokens[b] = tuple(tokens[:(j + 1) * bs])
+                parent = b
+        self.seqs[seq] = [blocks, len(tokens)]
+        self.prefix_hits += len(hits)
+        self.prefix_lookups += nfull
+        return OK, len(hits) * bs
 
     def fork(self, parent, child):
         if parent not in self.seqs:
@@ -66,7 +156,7 @@ class BlockManagerModel:
             return EINVAL
         blocks, n = self.seqs[parent]
         for b in blocks:
-            self.rc[b] += 1
+            self._hold(b)
         self.seqs[child] = [list(blocks), n]
         return OK
 
@@ -79,7 +169,7 @@ class BlockManagerModel:
         if nblocks * self.block_size > n:
             return EINVAL
         for b in blocks[:nblocks]:
-            self.rc[b] += 1
+            self._hold(b)
         self.seqs[dst] = [list(blocks[:nblocks]), nblocks * self.block_size]
         return OK
 
@@ -92,20 +182,18 @@ class BlockManagerModel:
         off = n % self.block_size
         status, cs, cd = OK, -1, -1
         if off == 0:
-            if not self.free:
+            if self._available() == 0:
                 self.alloc_failures += 1
                 return ENOBLOCKS, -1, -1, -1
-            blk = self.free.pop()
-            self.rc[blk] = 1
+            blk = self._take()
             blocks.append(blk)
         else:
             last = blocks[-1]
             if self.rc[last] > 1:
-                if not self.free:
+                if self._available() == 0:
                     self.alloc_failures += 1
                     return ENOBLOCKS, -1, -1, -1
-                blk = self.free.pop()
-                self.rc[blk] = 1
+                blk = self._take()
                 self.rc[last] -= 1
                 blocks[-1] = blk
                 self.cow_copies += 1
@@ -122,17 +210,12 @@ class BlockManagerModel:
             return ENOSEQ, -1, -1
         if num_tokens < 0:
             return EINVAL, -1, -1
-        saved = (list(self.free), list(self.rc), list(self.seqs[seq][0]), self.seqs[seq][1],
-                 self.cow_copies)
+        snap = self.snapshot()
         first = (OK, -1, -1)
         for i in range(num_tokens):
             st, _, cs, cd = self.append_slot(seq)
             if st < 0:
-                failures = self.alloc_failures
-                self.free, self.rc = saved[0], saved[1]
-                self.seqs[seq] = [saved[2], saved[3]]
-                self.cow_copies = saved[4]
-                self.alloc_failures = failures
+                self.restore(snap)
                 return st, -1, -1
             if i == 0:
                 first = (st, cs, cd)
@@ -143,9 +226,7 @@ class BlockManagerModel:
             return ENOSEQ
         blocks, _ = self.seqs.pop(seq)
         for b in reversed(blocks):
-            self.rc[b] -= 1
-            if self.rc[b] == 0:
-                self.free.append(b)
+            self._release(b)
         return OK
 
     def table(self, seq):
@@ -166,6 +247,11 @@ class BlockManagerModel:
     def stats(self):
         used = sum(1 for r in self.rc if r > 0)
         shared = sum(1 for r in self.rc if r > 1)
-        return {"used": used, "free": len(self.free), "shared": shared,
+        return {"used": used, "free": self._available(), "shared": shared,
                 "cow_copies": self.cow_copies, "alloc_failures": self.alloc_failures,
-                "num_seqs": len(self.seqs)}
+                "num_seqs": len(self.seqs), "prefix_hits": self.prefix_hits,
+                "prefix_lookups": self.prefix_lookups}
+
+    def prefix_stats(self):
+        return {"cached_blocks": len(self.cache), "cached_unheld": len(self.released),
+                "hits": self.prefix_hits, "lookups": self.prefix_lookups}

@@ -17,7 +17,9 @@ import numpy as np
 
 from ._lib import lib, check, PKV_ENOBLOCKS, PagedKVError
 
-STAT_KEYS = ("used", "free", "shared", "cow_copies", "alloc_failures", "num_seqs")
+STAT_KEYS = ("used", "free", "shared", "cow_copies", "alloc_failures", "num_seqs",
+             "prefix_hits", "prefix_lookups")
+PREFIX_KEYS = ("cached_blocks", "cached_unheld", "hits", "lookups")
 
 
 def _p(a: np.ndarray, ctype):
@@ -137,6 +139,26 @@ class BlockManager:
                                       _p(tables, ctypes.c_int32), width,
                                       _p(lens, ctypes.c_int32)), "build_tables")
         return tables[:n], lens[:n]
+
+    def add_seq_cached_status(self, seq: int, token_ids):
+        """(status, cached tokens) of adding a prompt through the prefix cache."""
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        n = ctypes.c_int(0)
+        st = lib.pkv_bm_add_seq_cached(self._h, seq, _p(t, ctypes.c_int32) if t.size else None,
+                                       int(t.size), ctypes.byref(n))
+        return st, (n.value if st >= 0 else 0)
+
+    def add_seq_cached(self, seq: int, token_ids) -> int:
+        """Adds a prompt, reusing cached blocks of its leading full blocks (P1 §7.4; P3
+        §2.2.8); returns how many leading tokens were already cached."""
+        st, n = self.add_seq_cached_status(seq, token_ids)
+        check(st, "add_seq_cached")
+        return n
+
+    def prefix_stats(self) -> dict:
+        out = np.zeros(4, dtype=np.int64)
+        check(lib.pkv_bm_prefix_stats(self._h, _p(out, ctypes.c_int64)), "prefix_stats")
+        return {k: int(out[i]) for i, k in enumerate(PREFIX_KEYS)}
 
     def refcount(self, block: int) -> int:
         return check(lib.pkv_bm_refcount(self._h, block), "refcount")

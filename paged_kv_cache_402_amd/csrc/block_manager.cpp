@@ -17,6 +17,8 @@
 // a caller-given order, so results are reproducible id for id.
 #include <cstdint>
 #include <cstring>
+#include <list>
+#include <string>
 #include <unordered_map>
 #include <vector>
 
@@ -31,31 +33,102 @@ struct pkv_bm {
   int num_blocks = 0;
   int block_size = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
-  std::vector<int32_t> rc;          // refcount per block; 0 = free
+  std::vector<int32_t> rc;          // refcount per block; 0 = free or cached
   std::unordered_map<int64_t, Seq> seqs;
   int64_t shared = 0;               // blocks with rc > 1
   int64_t cow_copies = 0;
   int64_t alloc_failures = 0;
 
+  // Prefix cache (P1 §7.4; P3 §2.2.8): a full prompt block is registered under its key: the
+  // block before it (its id and hand-out generation, or -1) followed by its block_size token
+  // ids. By induction the key names the whole token prefix up to that block exactly; the
+  // generation, bumped each time a block is handed out, keeps keys that name an evicted
+  // block's old contents from ever matching again. Registered blocks whose refcount falls to
+  // zero stay cached, in release order; they are handed out again only when the free stack is
+  // empty, oldest release first, and then leave the cache.
+  std::unordered_map<std::string, int32_t> cache;
+  std::vector<uint32_t> gen;                        // hand-outs of each block so far
+  std::vector<std::string> block_key;               // "" when the block is not registered
+  std::list<int32_t> lru;                           // cached blocks with rc == 0, oldest first
+  std::vector<std::list<int32_t>::iterator> lru_it;
+  std::vector<char> in_lru;
+  int64_t prefix_hits = 0;                          // cached blocks reused by add_seq_cached
+  int64_t prefix_lookups = 0;                       // full prompt blocks looked up
+
+  size_t available() const { return free_stack.size() + lru.size(); }
+
+  void lru_push_back(int32_t b) {
+    lru_it[b] = lru.insert(lru.end(), b);
+    in_lru[b] = 1;
+  }
+  void lru_push_front(int32_t b) {
+    lru_it[b] = lru.insert(lru.begin(), b);
+    in_lru[b] = 1;
+  }
+  void lru_erase(int32_t b) {
+    lru.erase(lru_it[b]);
+    in_lru[b] = 0;
+  }
   void inc(int32_t b) {
+    if (rc[b] == 0 && in_lru[b]) lru_erase(b);  // a cached block comes back into use
     if (++rc[b] == 2) ++shared;
   }
   void dec(int32_t b) {
     if (rc[b]-- == 2) --shared;
-    if (rc[b] == 0) free_stack.push_back(b);
+    if (rc[b] == 0) {
+      if (!block_key[b].empty())
+        lru_push_back(b);
+      else
+        free_stack.push_back(b);
+    }
   }
-  int32_t take() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+  // Hands out a block: the top of the free stack, else the cached block released longest ago
+  // (it leaves the cache; its key goes to *evicted so an undo can restore it).
+  int32_t take(std::string* evicted = nullptr) {
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+      if (evicted) evicted->clear();
+    } else {
+      b = lru.front();
+      lru_erase(b);
+      std::string key;
+      key.swap(block_key[b]);
+      cache.erase(key);
+      if (evicted) *evicted = std::move(key);
+    }
     rc[b] = 1;
+    ++gen[b];
     return b;
   }
-  // Returns a block taken last back to the top of the free stack.
-  void untake(int32_t b) {
+  // Undoes the last take(): the block goes back where it came from.
+  void untake(int32_t b, const std::string& evicted) {
     rc[b] = 0;
-    free_stack.push_back(b);
+    --gen[b];
+    if (evicted.empty()) {
+      free_stack.push_back(b);
+    } else {
+      block_key[b] = evicted;
+      cache[evicted] = b;
+      lru_push_front(b);
+    }
   }
 };
+
+namespace {
+
+std::string block_key_of(const pkv_bm* bm, int32_t parent, const int32_t* tokens) {
+  const int bs = bm->block_size;
+  const uint32_t g = parent >= 0 ? bm->gen[parent] : 0u;
+  std::string k((size_t)(bs + 2) * sizeof(int32_t), '\0');
+  std::memcpy(&k[0], &parent, sizeof(int32_t));
+  std::memcpy(&k[sizeof(int32_t)], &g, sizeof(uint32_t));
+  std::memcpy(&k[2 * sizeof(int32_t)], tokens, (size_t)bs * sizeof(int32_t));
+  return k;
+}
+
+}  // namespace
 
 namespace {
 
@@ -64,6 +137,7 @@ struct AppendUndo {
   pkv_bm::Seq* seq;
   int kind;         // 0: wrote in place, 1: fresh block appended, 2: copy-on-write
   int32_t src, dst;
+  std::string evicted;  // cache key of dst if taking it evicted a cached block
 };
 
 int append_one(pkv_bm* bm, int64_t id, int32_t* slot, AppendUndo* undo) {
@@ -77,22 +151,22 @@ int append_one(pkv_bm* bm, int64_t id, int32_t* slot, AppendUndo* undo) {
   undo->seq = &s;
   undo->src = undo->dst = -1;
   if (off == 0) {
-    if (bm->free_stack.empty()) {
+    if (bm->available() == 0) {
       ++bm->alloc_failures;
       return pkv::fail(PKV_ENOBLOCKS, "append_slot: pool exhausted");
     }
-    blk = bm->take();
+    blk = bm->take(&undo->evicted);
     s.blocks.push_back(blk);
     undo->kind = 1;
     undo->dst = blk;
   } else {
     int32_t last = s.blocks.back();
     if (bm->rc[last] > 1) {
-      if (bm->free_stack.empty()) {
+      if (bm->available() == 0) {
         ++bm->alloc_failures;
         return pkv::fail(PKV_ENOBLOCKS, "append_slot: pool exhausted (copy-on-write)");
       }
-      blk = bm->take();
+      blk = bm->take(&undo->evicted);
       bm->dec(last);  // stays > 0: it was shared
       s.blocks.back() = blk;
       ++bm->cow_copies;
@@ -114,11 +188,11 @@ void undo_one(pkv_bm* bm, const AppendUndo& u) {
   --s.tokens;
   if (u.kind == 1) {
     s.blocks.pop_back();
-    bm->untake(u.dst);
+    bm->untake(u.dst, u.evicted);
   } else if (u.kind == 2) {
     s.blocks.back() = u.src;
     bm->inc(u.src);
-    bm->untake(u.dst);
+    bm->untake(u.dst, u.evicted);
     --bm->cow_copies;
   }
 }
@@ -136,6 +210,10 @@ pkv_bm* pkv_bm_create(int num_blocks, int block_size, const int32_t* free_order)
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->rc.assign(num_blocks, 0);
+  bm->block_key.assign(num_blocks, std::string());
+  bm->gen.assign(num_blocks, 0u);
+  bm->lru_it.resize(num_blocks);
+  bm->in_lru.assign(num_blocks, 0);
   bm->free_stack.resize(num_blocks);
   std::vector<char> seen(num_blocks, 0);
   for (int i = 0; i < num_blocks; ++i) {
@@ -158,9 +236,9 @@ int pkv_bm_add_seq(pkv_bm* bm, int64_t seq, int num_tokens) {
   if (!bm || num_tokens < 0) return pkv::fail(PKV_EINVAL, "add_seq: bad argument");
   if (bm->seqs.count(seq)) return pkv::fail(PKV_EINVAL, "add_seq: sequence %lld exists", (long long)seq);
   size_t need = ((size_t)num_tokens + bm->block_size - 1) / bm->block_size;
-  if (need > bm->free_stack.size()) {
+  if (need > bm->available()) {
     ++bm->alloc_failures;
-    return pkv::fail(PKV_ENOBLOCKS, "add_seq: %zu blocks needed, %zu free", need, bm->free_stack.size());
+    return pkv::fail(PKV_ENOBLOCKS, "add_seq: %zu blocks needed, %zu free", need, bm->available());
   }
   pkv_bm::Seq s;
   s.blocks.reserve(need + 1);
@@ -309,14 +387,72 @@ int pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
 
 int pkv_bm_stats(const pkv_bm* bm, int64_t out[8]) {
   if (!bm || !out) return pkv::fail(PKV_EINVAL, "stats: bad argument");
-  out[0] = bm->num_blocks - (int64_t)bm->free_stack.size();
-  out[1] = (int64_t)bm->free_stack.size();
+  out[0] = bm->num_blocks - (int64_t)bm->available();
+  out[1] = (int64_t)bm->available();
   out[2] = bm->shared;
   out[3] = bm->cow_copies;
   out[4] = bm->alloc_failures;
   out[5] = (int64_t)bm->seqs.size();
-  out[6] = 0;
-  out[7] = 0;
+  out[6] = bm->prefix_hits;
+  out[7] = bm->prefix_lookups;
+  return pkv::ok();
+}
+
+int pkv_bm_add_seq_cached(pkv_bm* bm, int64_t seq, const int32_t* token_ids, int num_tokens,
+                          int* num_cached_tokens) {
+  if (!bm || num_tokens < 0 || (num_tokens > 0 && !token_ids))
+    return pkv::fail(PKV_EINVAL, "add_seq_cached: bad argument");
+  if (bm->seqs.count(seq)) return pkv::fail(PKV_EINVAL, "add_seq_cached: sequence %lld exists", (long long)seq);
+  const int bs = bm->block_size;
+  const int nfull = num_tokens / bs;
+  const size_t nblocks = ((size_t)num_tokens + bs - 1) / bs;
+  // longest run of leading full blocks already cached
+  std::vector<int32_t> hits;
+  int32_t parent = -1;
+  size_t hits_cached_free = 0;  // hits that sit in the cache unreferenced (not allocatable then)
+  for (int j = 0; j < nfull; ++j) {
+    auto it = bm->cache.find(block_key_of(bm, parent, token_ids + (size_t)j * bs));
+    if (it == bm->cache.end()) break;
+    hits.push_back(it->second);
+    if (bm->rc[it->second] == 0) ++hits_cached_free;
+    parent = it->second;
+  }
+  const size_t need = nblocks - hits.size();
+  if (need > bm->available() - hits_cached_free) {
+    ++bm->alloc_failures;
+    return pkv::fail(PKV_ENOBLOCKS, "add_seq_cached: %zu blocks needed, %zu free", need,
+                     bm->available() - hits_cached_free);
+  }
+  pkv_bm::Seq s;
+  s.blocks.reserve(nblocks + 1);
+  for (int32_t b : hits) {
+    bm->inc(b);  // leaves the released-block list if it was there
+    s.blocks.push_back(b);
+  }
+  for (size_t j = hits.size(); j < nblocks; ++j) {
+    const int32_t b = bm->take();
+    s.blocks.push_back(b);
+    if ((int)j < nfull) {  // register the new full block under its prefix
+      std::string key = block_key_of(bm, parent, token_ids + j * bs);
+      bm->cache[key] = b;
+      bm->block_key[b] = std::move(key);
+      parent = b;
+    }
+  }
+  s.tokens = num_tokens;
+  bm->seqs.emplace(seq, std::move(s));
+  bm->prefix_hits += (int64_t)hits.size();
+  bm->prefix_lookups += nfull;
+  if (num_cached_tokens) *num_cached_tokens = (int)hits.size() * bs;
+  return pkv::ok();
+}
+
+int pkv_bm_prefix_stats(const pkv_bm* bm, int64_t out[4]) {
+  if (!bm || !out) return pkv::fail(PKV_EINVAL, "prefix_stats: bad argument");
+  out[0] = (int64_t)bm->cache.size();
+  out[1] = (int64_t)bm->lru.size();
+  out[2] = bm->prefix_hits;
+  out[3] = bm->prefix_lookups;
   return pkv::ok();
 }
 

@@ -17,6 +17,8 @@ from hypothesis import given, settings, strategies as st
 
 from oracle.block_manager_model import BlockManagerModel
 
+PKV_ENOBLOCKS = -3
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "block_table_worked_example.json")
 
 
@@ -32,8 +34,10 @@ def _same_state(cpp, model):
         assert cpp.refcount(b) == model.refcount(b)
     s = cpp.stats()
     ms = model.stats()
-    for k in ("used", "free", "shared", "cow_copies", "alloc_failures", "num_seqs"):
+    for k in ("used", "free", "shared", "cow_copies", "alloc_failures", "num_seqs",
+              "prefix_hits", "prefix_lookups"):
         assert s[k] == ms[k], k
+    assert cpp.prefix_stats() == model.prefix_stats()
 
 
 def test_worked_example_p3_2_2_3():
@@ -109,7 +113,16 @@ def test_bad_free_order_and_unknown_ids():
         bm.refcount(4)
 
 
-OPS = st.lists(st.tuples(st.integers(0, 6), st.integers(0, 10 ** 6)), min_size=1, max_size=120)
+OPS = st.lists(st.tuples(st.integers(0, 7), st.integers(0, 10 ** 6)), min_size=1, max_size=120)
+
+
+def _no_false_sharing(model, seq, toks):
+    """Every cached block a sequence starts with ends exactly the token prefix it holds."""
+    blocks, _ = model.table(seq)
+    bs = model.block_size
+    for j, b in enumerate(blocks[:len(toks) // bs]):
+        if b in model.prefix_tokens:
+            assert model.prefix_tokens[b] == tuple(toks[:(j + 1) * bs])
 
 
 @settings(max_examples=150, deadline=None)
@@ -149,20 +162,28 @@ def test_matches_reference_model(nb, bs, seed, ops):
         elif op == 6:
             n = r % (2 * bs + 2)
             assert cpp.extend_status(pick, n) == model.extend(pick, n)
+        elif op == 7:
+            # prompts from a 2-token vocabulary, so leading blocks repeat and hit the cache
+            n = r % (3 * bs + 2)
+            toks = [(r >> (i % 20)) & 1 for i in range(n)]
+            got = cpp.add_seq_cached_status(next_id, toks)
+            exp = model.add_seq_cached(next_id, toks)
+            assert got == exp
+            if next_id in model.seqs:
+                ids.append(next_id)
+                _no_false_sharing(model, next_id, toks)
+            next_id += 1
         else:
             batch = [ids[(r + i) % len(ids)] for i in range(r % 3 + 1)] if ids else []
             if batch:
-                # the model applies one by one; on failure it is rolled back by replaying
-                snapshot = (list(model.free), list(model.rc),
-                            {k: [list(v[0]), v[1]] for k, v in model.seqs.items()},
-                            model.cow_copies)
+                # the model applies one by one; on failure it is rolled back to a snapshot
+                snap = model.snapshot()
                 res = [model.append_slot(s) for s in batch]
                 failed = any(x[0] < 0 for x in res)
                 if failed:
-                    model.free, model.rc, model.seqs, model.cow_copies = (
-                        snapshot[0], snapshot[1], snapshot[2], snapshot[3])
-                    model.alloc_failures = model.alloc_failures - sum(
-                        1 for x in res if x[0] < 0) + 1
+                    failures = model.alloc_failures
+                    model.restore(snap)
+                    model.alloc_failures = failures - sum(1 for x in res if x[0] < 0) + 1
                     with pytest.raises(Exception):
                         cpp.append_slots(batch)
                 else:
@@ -170,3 +191,74 @@ def test_matches_reference_model(nb, bs, seed, ops):
                     assert slots.tolist() == [x[1] for x in res]
                     assert pairs.tolist() == [[x[2], x[3]] for x in res if x[0] == 1]
         _same_state(cpp, model)
+
+
+# ------------------------------------------------------------------------------------------
+# prefix caching (P1 §7.4; P3 §2.2.8, §2.2.13)
+# ------------------------------------------------------------------------------------------
+
+def test_prefix_cache_reuses_a_shared_system_prompt():
+    bm = _bm(64, 4)
+    system = list(range(100, 112))                      # 3 full blocks
+    assert bm.add_seq_cached(0, system + [1, 2]) == 0     # cold: nothing cached
+    t0, _ = bm.table(0)
+    assert bm.add_seq_cached(1, system + [7, 8, 9]) == 12
+    t1, _ = bm.table(1)
+    assert t1[:3] == t0[:3] and t1[3] != t0[3]
+    for b in t0[:3]:
+        assert bm.refcount(b) == 2
+    st = bm.stats()
+    assert (st["prefix_hits"], st["prefix_lookups"]) == (3, 6)
+    # a different first token shares nothing
+    assert bm.add_seq_cached(2, [999] + system[1:]) == 0
+
+
+def test_prefix_cache_keeps_released_blocks_and_evicts_oldest_last():
+    bm = _bm(6, 2)
+    assert bm.add_seq_cached(0, [1, 2, 3, 4]) == 0        # blocks cached: [1,2] and [1,2][3,4]
+    blocks0, _ = bm.table(0)
+    bm.free_seq(0)
+    assert bm.stats()["free"] == 6                        # cached but unheld counts as free
+    assert bm.prefix_stats()["cached_unheld"] == 2
+    assert bm.add_seq_cached(1, [1, 2, 3, 4, 5]) == 4     # both come back from the cache
+    assert bm.table(1)[0][:2] == blocks0
+    bm.free_seq(1)
+    # fill the pool: the free blocks go first, then the cached ones, released-longest-ago first
+    bm.add_seq(2, 2 * 4)
+    assert bm.prefix_stats()["cached_blocks"] == 2
+    bm.add_seq(3, 2)
+    assert bm.prefix_stats()["cached_blocks"] == 1
+    assert bm.add_seq_status(4, 4) == PKV_ENOBLOCKS
+
+
+def test_prefix_cache_never_matches_an_evicted_parent():
+    """A cached block's key names its predecessor's hand-out, so once the predecessor is
+    evicted and refilled with other tokens, its old successor can no longer be matched."""
+    bm = _bm(3, 1)
+    bm.add_seq_cached(0, [5, 6])                          # A=[5], B=[5][6]
+    a, b = bm.table(0)[0]
+    bm.free_seq(0)                                        # released: B first, then A
+    bm.add_seq(1, 1)                                      # takes the free block
+    bm.add_seq(2, 1)                                      # evicts B (released longest ago)
+    bm.free_seq(1)
+    bm.free_seq(2)
+    model = BlockManagerModel(3, 1)
+    model.add_seq_cached(0, [5, 6])
+    model.free_seq(0)
+    model.add_seq(1, 1)
+    model.add_seq(2, 1)
+    model.free_seq(1)
+    model.free_seq(2)
+    assert bm.add_seq_cached_status(3, [5, 6]) == model.add_seq_cached(3, [5, 6])
+    _no_false_sharing(model, 3, [5, 6])
+    _same_state(bm, model)
+
+
+def test_prefix_cache_failure_is_atomic():
+    bm = _bm(4, 2)
+    bm.add_seq_cached(0, [1, 1, 2, 2])
+    before = (bm.stats(), bm.prefix_stats(), bm.table(0))
+    assert bm.add_seq_cached_status(1, [1, 1, 3, 3, 4, 4, 5, 5]) == (PKV_ENOBLOCKS, 0)
+    after = (bm.stats(), bm.prefix_stats(), bm.table(0))
+    assert after[0]["alloc_failures"] == before[0]["alloc_failures"] + 1
+    assert after[1] == before[1] and after[2] == before[2]

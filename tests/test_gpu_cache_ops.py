@@ -212,3 +212,45 @@ def test_longtail_parallel_sampling_step():
     ref = oracle(step)
     from tests.gpu_util import half_ulp
     assert (np.abs(got16 - ref) <= GATE["f16"] + half_ulp(ref, "f16")).all()
+
+
+def test_prefix_cached_requests_decode_over_shared_blocks():
+    """P1 §7.4 / P3 §2.2.8: a second request with the same system prompt reuses the cached
+    blocks and writes K/V only for its own tokens; both decode to the attention over their own
+    logically contiguous K/V."""
+    from oracle import paged_attention as ref_pa
+    P = pk()
+    rng = np.random.default_rng(77)
+    bs, H, d, NB = 16, 4, 128, 40
+    bm = P.BlockManager(NB, bs)
+    system = rng.integers(0, 50000, 48).tolist()                 # 3 full blocks
+    users = [rng.integers(0, 50000, n).tolist() for n in (10, 23)]
+    sys_k = gen.normal(rng, (48, H, d), "bf16")
+    sys_v = gen.normal(rng, (48, H, d), "bf16")
+    user_kv = [(gen.normal(rng, (len(u), H, d), "bf16"), gen.normal(rng, (len(u), H, d), "bf16"))
+               for u in users]
+    kd = to_dev(np.full((NB, H, bs, d), gen.nan_value("bf16"), np.uint16), "bf16")
+    vd = to_dev(np.full((NB, H, bs, d), gen.nan_value("bf16"), np.uint16), "bf16")
+    cached = []
+    for s, u in enumerate(users):
+        toks = system + u
+        c = bm.add_seq_cached(s, toks)
+        cached.append(c)
+        k_all = np.concatenate([sys_k, user_kv[s][0]])
+        v_all = np.concatenate([sys_v, user_kv[s][1]])
+        slots = bm.slots(s, c, len(toks) - c)
+        P.reshape_and_cache(to_dev(k_all[c:], "bf16"), to_dev(v_all[c:], "bf16"), kd, vd, i32(slots))
+    assert cached == [0, 48]
+    assert bm.stats()["prefix_hits"] == 3
+    tables, lens = bm.build_tables([0, 1], 8)
+    assert tables[0, :3].tolist() == tables[1, :3].tolist()
+    q = gen.normal(rng, (2, H, d), "bf16")
+    out = torch.empty((2, H, d), dtype=torch.float32, device="cuda")
+    P.paged_attention_decode(out, to_dev(q, "bf16"), kd, vd, i32(tables), i32(lens), 0.088)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for s in range(2):
+        k_all = np.concatenate([sys_k, user_kv[s][0]])
+        v_all = np.concatenate([sys_v, user_kv[s][1]])
+        ref = ref_pa.contiguous_attention(q[s], k_all, v_all, 0.088, "bf16")
+        assert max_err(got[s], ref) <= GATE["bf16"]
