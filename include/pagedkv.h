@@ -242,6 +242,37 @@ int pkv_bm_add_seq_cached(pkv_bm* bm, int64_t seq, const int32_t* token_ids, int
 /* out[0] registered blocks, [1] of them held by no sequence, [2] hits, [3] lookups. */
 int pkv_bm_prefix_stats(const pkv_bm* bm, int64_t out[4]);
 
+/* ------------------------------------------------------------------------------------------
+ * KV-pool sizing (P3 §2.2.5, §2.2.7). The pool is fixed at start-up from a memory fraction;
+ * this host-only helper turns the device memory, the weights and the model's KV shape into
+ * the num_blocks to pass to pkv_bm_create and to allocate the caches with, and into how many
+ * requests of a given context length fit at once. Integer arithmetic only.
+ * ------------------------------------------------------------------------------------------ */
+
+/* How utilization_ppm is applied. P3's worked figure (80 GB device, 40 GB of weights, 0.9 ->
+ * about 36 GB of pool) takes the fraction of what the weights leave: REMAINDER. DEVICE takes
+ * the fraction of the whole device as the process's cap, and the weights come out of it. */
+enum { PKV_UTIL_OF_REMAINDER = 0, PKV_UTIL_OF_DEVICE = 1 };
+
+/* device_bytes: memory of one GPU; weight_bytes: its weights; reserve_bytes: activations and
+ * workspaces kept out of the pool; utilization_ppm: the memory fraction in parts per million,
+ * in (0, 1000000]. One token's KV takes num_layers * 2 * num_kv_heads * head_dim * elem_bytes
+ * bytes (elem_bytes 1, 2 or 4); every layer has its own K and V cache of num_blocks blocks.
+ *   REMAINDER: pool = floor((device - weights - reserve) * ppm / 1e6)
+ *   DEVICE:    pool = floor(device * ppm / 1e6) - weights - reserve
+ * out[0] pool bytes, [1] KV bytes per token (all layers), [2] bytes per block (all layers),
+ * [3] num_blocks = floor(pool / out[2]), [4] blocks per request = ceil(context_tokens /
+ * block_size), [5] requests served at once = floor(out[3] / out[4]), [6] bytes of one layer's
+ * K cache (= V cache) [num_blocks][num_kv_heads][block_size][head_dim], [7] requests served
+ * at once if each reserved max_model_len tokens contiguously = floor(pool / (out[1] *
+ * max_model_len)). PKV_EINVAL for out-of-range arguments or num_blocks * block_size >=
+ * 2^31 (slot ids are int32); PKV_ENOBLOCKS if the pool holds no block (out[0], [1], [2], [4]
+ * are still filled). */
+int pkv_kv_pool_plan(int64_t device_bytes, int64_t weight_bytes, int64_t reserve_bytes,
+                     int32_t utilization_ppm, int utilization_of, int num_layers,
+                     int num_kv_heads, int head_dim, int elem_bytes, int block_size,
+                     int context_tokens, int max_model_len, int64_t out[8]);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,8 @@ SIGNATURES = {
     "pkv_bm_stats": (c_int, [c_void_p, P_i64]),
     "pkv_bm_add_seq_cached": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),
     "pkv_bm_prefix_stats": (c_int, [c_void_p, P_i64]),
+    "pkv_kv_pool_plan": (c_int, [c_int64, c_int64, c_int64, ctypes.c_int32, c_int, c_int, c_int,
+                                 c_int, c_int, c_int, c_int, c_int, P_i64]),
 }
 
 # status codes (include/pagedkv.h)
