@@ -46,11 +46,20 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
     p.add_argument("--partition", type=int, default=512)
+    p.add_argument("--grid", choices=("list", "full"), default="list",
+                   help="per-partition pass over the host work list (one workgroup per "
+                        "partition that holds tokens) or over the full partition x sequence grid")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain block copy of known size (HBM counter calibration)")
+    p.add_argument("--warm", action="store_true",
+                   help="time back-to-back steps by wall clock, leaving the previous step's "
+                        "KV in L2 and the 256 MB memory-side cache (default: read a 1 GiB "
+                        "buffer before every step and time the step alone with HIP events)")
+    p.add_argument("--fork-tree", action="store_true",
+                   help="only count the blocks branch trees hold (host block manager, no GPU)")
     return p.parse_args()
 
 
@@ -308,6 +317,65 @@ def copy_probe(pk, torch, dev):
                       "bytes_written_per_launch": per, "launches": 5}), flush=True)
 
 
+def fork_tree_report(pk):
+    """Blocks held by branch trees on the block manager against private copies per branch
+    (every branch holding ceil(tokens / block_size) blocks of its own). Prompts of
+    Geometric(1/200) tokens clipped to [1, 2048] (the long-tail length mix), block size 16;
+    parallel sampling: n branches of 128 tokens; beam search: `width` beams for 128 steps.
+    saving = 1 - sum over steps of blocks held / sum of private blocks, over the steps where
+    more than one branch is alive; peak = the largest per-step count of each."""
+    from workloads import traces
+    rng = np.random.default_rng(402500)
+    prompts = np.clip(rng.geometric(1 / 200, size=32), 1, 2048)
+    bs = 16
+    rows = []
+    settings = [("parallel_sampling", n) for n in (2, 4, 8)] + [("beam_search", w)
+                                                                  for w in (2, 4, 8)]
+    for kind, n in settings:
+        held = private = peak_h = peak_p = steps = 0
+        t_host = 0.0
+        for i, P in enumerate(prompts.tolist()):
+            trng = np.random.default_rng(402600 + i)
+            if kind == "parallel_sampling":
+                tr = traces.parallel_sampling_trace(trng, P, n, 128)
+            else:
+                tr = traces.beam_search_trace(trng, P, n, 128)
+            need = 4 * n * (-(-(P + 130) // bs)) + 8
+            bm = pk.BlockManager(need, bs)
+            bm.add_seq(tr.root, P)
+            live = {tr.root}
+            ntok = {tr.root: P}
+            for st in tr.steps:
+                t0 = time.perf_counter()
+                for s in st.frees:
+                    bm.free_seq(s)
+                for par, c in st.forks:
+                    bm.fork(par, c)
+                if st.appends:
+                    bm.append_slots(st.appends)
+                t_host += time.perf_counter() - t0
+                live -= set(st.frees)
+                for par, c in st.forks:
+                    live.add(c)
+                    ntok[c] = ntok[par]
+                for s in st.appends:
+                    ntok[s] += 1
+                if len(live) > 1:
+                    h = bm.stats()["used"]
+                    pv = sum(-(-ntok[s] // bs) for s in live)
+                    held, private, steps = held + h, private + pv, steps + 1
+                    peak_h, peak_p = max(peak_h, h), max(peak_p, pv)
+            bm.close()
+        rows.append({"tree": kind, "branches": n, "prompts": len(prompts),
+                     "saving": round(1 - held / private, 4),
+                     "saving_at_peak": round(1 - peak_h / peak_p, 4),
+                     "mean_blocks_held": round(held / steps, 1),
+                     "mean_blocks_private": round(private / steps, 1),
+                     "host_us_per_step": round(t_host / max(1, steps) * 1e6, 2)})
+    print(json.dumps({"fork_tree": True, "block_size": bs,
+                      "prompt_mean": round(float(prompts.mean()), 1), "rows": rows}), flush=True)
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -315,6 +383,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), flush=True)
         sys.exit(2)
+    if args.fork_tree:
+        import paged_kv_cache_402_amd as pk
+        fork_tree_report(pk)
+        return
     import torch
     import paged_kv_cache_402_amd as pk
     from workloads import gen
@@ -328,6 +400,11 @@ def main():
     case = st["case"]
     part = args.partition
     bytes_ = byte_model(case, part)
+    work = None
+    if args.grid == "list":
+        items = pk.decode_work_list(case.seq_lens, case.table_width, case.block_size, part)
+        work = torch.from_numpy(items).to(dev)
+        bytes_["decode_kernel"] += 4 * int(items.shape[0])     # one item read per launch
     ws = torch.empty(max(1, pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads,
                                                       case.table_width, case.block_size,
                                                       case.head_dim, part)),
@@ -349,7 +426,8 @@ def main():
             ev[i][1].record()
         # paged_attention_decode's two launches, called apart so each has its own events
         pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
-                                      st["lens"], case.scale, partition_size=part, workspace=ws)
+                                      st["lens"], case.scale, partition_size=part, workspace=ws,
+                                      work_list=work)
         if i is not None:
             ev[i][2].record()
         pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width, ws,
@@ -361,13 +439,23 @@ def main():
     for _ in range(W):
         step()
     torch.cuda.synchronize()
-    log("timing %d steps" % K)
+    # Each layer of a model reads its own KV once per step, so between two reads of one
+    # layer's KV the other layers' KV has passed through the caches. Reading (not writing:
+    # dirty lines would be written back inside the timed step) 1 GiB of other data before
+    # every step gives the step the same cold L2 and memory-side cache.
+    evict = None if args.warm else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    evict_sum = torch.zeros((), dtype=torch.float32, device=dev)
+    log("timing %d steps%s" % (K, "" if args.warm else " (1 GiB read before each)"))
     t0 = time.perf_counter()
     for i in range(K):
+        if evict is not None:
+            torch.sum(evict, dim=0, out=evict_sum)
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
+    ms_wall = (t1 - t0) * 1e3 / K
+    # cold: the step's own span between its first and last event (the eviction sits before it)
+    ms_step = ms_wall if args.warm else float(np.mean([e[4].elapsed_time(e[3]) for e in ev]))
     t_cw = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     t_cb = float(np.mean([e[4].elapsed_time(e[0]) for e in ev]))
     t_dec = [e[1].elapsed_time(e[2]) for e in ev]
@@ -388,6 +476,10 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_step, 5),
+        "timing": "wall clock over back-to-back steps (warm caches)" if args.warm else
+                  ("HIP events around each step, 1 GiB read before each (cold L2 and "
+                   "memory-side cache); wall clock incl. the eviction reads %.4f ms/step"
+                   % ms_wall),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -396,7 +488,7 @@ def main():
         "config": {"workload": case.name, "num_seqs": case.num_seqs,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
-                   "kv_dtype": case.dtype, "partition_size": part,
+                   "kv_dtype": case.dtype, "partition_size": part, "grid": args.grid,
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),
                    "num_blocks": case.num_blocks, "parallelism": "single GPU"},

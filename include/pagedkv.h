@@ -133,6 +133,41 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
                                int max_blocks_per_seq, int partition_size,
                                const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Work list of the per-partition pass, built on the host from host seq_lens: one item per
+ * (sequence b, context partition p) that holds tokens, item = (b << 16) | p as int32 bits
+ * (a length-0 sequence has one item, p = 0, that writes its zero row). Lengths are clamped
+ * to [0, max_blocks_per_seq * block_size] as the kernel clamps them. Order: the full
+ * partitions in (sequence, partition) order, then every sequence's last, shorter partition,
+ * longest first. With work_list NULL returns the item count; otherwise writes the items
+ * (capacity >= count, else PKV_EINVAL) and returns the count. Negative on bad arguments. */
+int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
+                         int block_size, int partition_size, int32_t* work_list, int capacity);
+
+/* pkv_paged_attention_decode / _partitions with the per-partition pass launched over a work
+ * list (device int32 [work_items], from pkv_decode_work_list) instead of the full
+ * (partition, sequence) grid: one workgroup per (KV head, item), so no workgroup is spent on
+ * partitions past a sequence's end, and the short last partitions run at the end of the
+ * launch. The list must hold every partition of every sequence exactly once (the merge pass
+ * reads all of them); items naming a sequence >= num_seqs or a partition past the
+ * sequence's end are skipped. Every partition computes exactly what it computes in the
+ * full-grid launch, so the output is bitwise the same. */
+int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, const void* k_cache,
+                                    const void* v_cache, int kv_dtype,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int partition_size, const int32_t* work_list,
+                                    int work_items, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
+                                        const void* k_cache, const void* v_cache, int kv_dtype,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int num_blocks,
+                                        int max_blocks_per_seq, float scale, int partition_size,
+                                        const int32_t* work_list, int work_items, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Cache write (P1 §4.3; P3 §2.2.2-§2.2.3): token t's K and V rows ([num_kv_heads][head_dim],
  * contiguous, t-major) are copied bit for bit to slot slot_mapping[t] of k_cache / v_cache.
  * A negative slot skips the token. Slots must be distinct. */

@@ -29,6 +29,16 @@ SIGNATURES = {
                                                c_void_p, c_size_t, c_void_p]),
     "pkv_paged_attention_reduce": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_decode_work_list": (c_int, [P_i32, c_int, c_int, c_int, c_int, P_i32, c_int]),
+    "pkv_paged_attention_decode_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                                c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                                c_int, c_int, c_int, c_int, c_float, c_int,
+                                                c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attention_partitions_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
+                                                    c_void_p, c_int, c_void_p, c_void_p, c_int,
+                                                    c_int, c_int, c_int, c_int, c_int, c_int,
+                                                    c_float, c_int, c_void_p, c_int, c_void_p,
+                                                    c_size_t, c_void_p]),
     "pkv_reshape_and_cache": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                       c_int, c_int, c_int, c_int, c_int, c_void_p]),
     "pkv_copy_blocks": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,

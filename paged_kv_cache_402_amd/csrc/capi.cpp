@@ -4,8 +4,10 @@
 
 #include <cstdarg>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "errors.h"
 #include "launch.h"
@@ -117,6 +119,8 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.pmax = (int)pmax;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.out_dtype = out_dtype;
+  a.work = nullptr;
+  a.work_items = 0;
   pl->group = group;
   pl->ws_needed = need;
   return ok();
@@ -157,6 +161,98 @@ int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, cons
   if (st != PKV_OK || num_seqs == 0) return st;
   return hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
                     "decode partitions launch");
+}
+
+int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
+                         int block_size, int partition_size, int32_t* work_list, int capacity) {
+  if (partition_size == 0) partition_size = 512;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "work_list: num_seqs %d out of range", num_seqs);
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_EINVAL, "work_list: block_size must be a power of two in [8, 256]");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "work_list: max_blocks_per_seq out of range");
+  if (partition_size < 32 || partition_size > 2048 || partition_size % 32 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PKV_EINVAL, "work_list: bad partition_size");
+  if (num_seqs > 0 && !seq_lens) return fail(PKV_EINVAL, "work_list: null seq_lens");
+  const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+  if ((cap_tokens + partition_size - 1) / partition_size > 65535)
+    return fail(PKV_EINVAL, "work_list: too many partitions per sequence");
+  // full partitions in (sequence, partition) order, then every sequence's last, shorter
+  // partition, longest first (ties in sequence order): the short items end the launch
+  std::vector<uint32_t> full;
+  std::vector<std::pair<int, uint32_t>> tail;  // (-tokens, item)
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t L = std::min<int64_t>(std::max(seq_lens[b], 0), cap_tokens);
+    const int64_t np = L == 0 ? 1 : (L + partition_size - 1) / partition_size;
+    for (int64_t p = 0; p < np; ++p) {
+      const int64_t n = std::min<int64_t>(partition_size, L - p * partition_size);
+      const uint32_t item = ((uint32_t)b << 16) | (uint32_t)p;
+      if (n == partition_size) full.push_back(item);
+      else tail.emplace_back(-(int)n, item);
+    }
+  }
+  std::stable_sort(tail.begin(), tail.end(),
+                   [](const std::pair<int, uint32_t>& x, const std::pair<int, uint32_t>& y) {
+                     return x.first < y.first;
+                   });
+  const int64_t total = (int64_t)full.size() + (int64_t)tail.size();
+  if (total > INT32_MAX / 8) return fail(PKV_EINVAL, "work_list: too many items");
+  if (work_list == nullptr) return (int)total;     // size query
+  if (capacity < total) return fail(PKV_EINVAL, "work_list: %lld items, capacity %d", (long long)total, capacity);
+  int64_t i = 0;
+  for (uint32_t it : full) work_list[i++] = (int32_t)it;
+  for (const auto& t : tail) work_list[i++] = (int32_t)t.second;
+  ok();
+  return (int)total;
+}
+
+static int partitions_list(const DecodePlan& pl0, int kv_dtype, int head_dim,
+                           const int32_t* work_list, int work_items, void* stream) {
+  if (work_items < 0) return fail(PKV_EINVAL, "decode: negative work_items");
+  if (work_items == 0) return ok();
+  if (!work_list) return fail(PKV_EINVAL, "decode: null work_list");
+  if ((int64_t)work_items * pl0.args.num_kv_heads > INT32_MAX)
+    return fail(PKV_EINVAL, "decode: work list too long");
+  DecodePlan pl = pl0;
+  pl.args.work = reinterpret_cast<const uint32_t*>(work_list);
+  pl.args.work_items = work_items;
+  return hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
+                    "decode partitions launch");
+}
+
+int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
+                                        const void* k_cache, const void* v_cache, int kv_dtype,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int num_blocks,
+                                        int max_blocks_per_seq, float scale, int partition_size,
+                                        const int32_t* work_list, int work_items, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
+}
+
+int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, const void* k_cache,
+                                    const void* v_cache, int kv_dtype,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int num_blocks, int max_blocks_per_seq,
+                                    float scale, int partition_size, const int32_t* work_list,
+                                    int work_items, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
 }
 
 int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens, int num_seqs,

@@ -133,9 +133,21 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   constexpr int NT = kDecodeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int kvh = blockIdx.x;
-  const int pi = blockIdx.y;
-  const int b = blockIdx.z;
+  int kvh, pi, b;
+  if (a.work != nullptr) {
+    // consecutive workgroups take the KV heads of one item, so with 8 KV heads each XCD of
+    // the round-robin dispatch keeps to one head
+    const unsigned item = blockIdx.x / (unsigned)a.num_kv_heads;
+    kvh = blockIdx.x - item * a.num_kv_heads;
+    const uint32_t w = a.work[item];
+    b = (int)(w >> 16);
+    pi = (int)(w & 0xFFFFu);
+    if (b >= a.num_seqs) return;
+  } else {
+    kvh = blockIdx.x;
+    pi = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -516,7 +528,8 @@ size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
 
 template <int DT, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.num_kv_heads, a.pmax, a.num_seqs);
+  const dim3 grid = a.work != nullptr ? dim3((unsigned)a.num_kv_heads * (unsigned)a.work_items)
+                                       : dim3(a.num_kv_heads, a.pmax, a.num_seqs);
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
   // Matrix-core scores for 16-bit data at G = 8, when a 16-token step stays inside one block
   // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured

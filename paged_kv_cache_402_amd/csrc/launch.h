@@ -27,12 +27,17 @@ struct DecodeArgs {
   int pmax;                    // partitions of the longest representable sequence
   float scale_log2;            // scale * log2(e): scores are kept in base-2 units
   int out_dtype;               // DType of out
+  // Optional list of (sequence << 16 | partition) items, one workgroup per (KV head, item);
+  // null: one workgroup per (KV head, partition, sequence) of the full pmax x B grid.
+  const uint32_t* work;
+  int work_items;
 };
 
 // Bytes of dynamic LDS one decode workgroup needs.
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part);
 
-// Launches the per-partition kernel (grid: Hkv x B x pmax).
+// Launches the per-partition kernel (grid: Hkv x pmax x B, or Hkv x work_items in one
+// dimension when a work list is given).
 hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_dim, int group,
                                     hipStream_t stream);
 // Launches the partition merge (grid: Hq x B); only multi-partition sequences do work.

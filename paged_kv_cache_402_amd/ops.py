@@ -6,6 +6,9 @@ HIP kernels of libpagedkv.so; nothing here computes on the host or falls back to
 """
 from __future__ import annotations
 
+import ctypes
+
+import numpy as np
 import torch
 
 from ._lib import lib, check
@@ -44,6 +47,32 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: 
                                               block_size, head_dim, partition_size))
 
 
+def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
+                     partition_size: int = DEFAULT_PARTITION) -> np.ndarray:
+    """Host work list of the per-partition pass (pkv_decode_work_list) from host lengths:
+    int32 items (sequence << 16 | partition), full partitions first, then the last partial
+    partitions longest first. Upload it and pass it as work_list=."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    lp = lens.ctypes.data_as(P_i32)
+    n = check(lib.pkv_decode_work_list(lp, lens.shape[0], max_blocks_per_seq, block_size,
+                                       partition_size, None, 0), "decode_work_list")
+    items = np.empty(n, dtype=np.int32)
+    check(lib.pkv_decode_work_list(lp, lens.shape[0], max_blocks_per_seq, block_size,
+                                   partition_size, items.ctypes.data_as(P_i32), n),
+          "decode_work_list")
+    return items
+
+
+def _work(work_list):
+    if work_list is None:
+        return None, 0
+    _i32(work_list, "work_list")
+    if work_list.dim() != 1:
+        raise ValueError("work_list must be 1-D")
+    return work_list.data_ptr(), work_list.shape[0]
+
+
 def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens):
     for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
@@ -76,32 +105,49 @@ def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                           partition_size: int = DEFAULT_PARTITION, workspace=None):
+                           partition_size: int = DEFAULT_PARTITION, workspace=None,
+                           work_list=None):
     """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
-    b's block table locates in the paged caches. Returns `out`."""
+    b's block table locates in the paged caches. With work_list (device int32 from
+    decode_work_list) the per-partition pass runs over that list. Returns `out`."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
     ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
-    check(lib.pkv_paged_attention_decode(
-        out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
-        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-        partition_size, ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
-        "paged_attention_decode")
+    wsp = ws.data_ptr() if ws is not None else None
+    if work_list is None:
+        check(lib.pkv_paged_attention_decode(
+            out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+            block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+            partition_size, wsp, wsb, _stream(q)), "paged_attention_decode")
+    else:
+        wl, wn = _work(work_list)
+        check(lib.pkv_paged_attention_decode_list(
+            out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+            block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+            partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_decode_list")
     return out
 
 
 def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                               partition_size: int = DEFAULT_PARTITION, workspace=None):
+                               partition_size: int = DEFAULT_PARTITION, workspace=None,
+                               work_list=None):
     """First pass of paged_attention_decode only (per-partition attention). Returns the
     workspace that paged_attention_reduce needs (None if no sequence spans two partitions)."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
     ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
-    check(lib.pkv_paged_attention_partitions(
-        out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
-        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-        partition_size, ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
-        "paged_attention_partitions")
+    wsp = ws.data_ptr() if ws is not None else None
+    if work_list is None:
+        check(lib.pkv_paged_attention_partitions(
+            out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+            block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+            partition_size, wsp, wsb, _stream(q)), "paged_attention_partitions")
+    else:
+        wl, wn = _work(work_list)
+        check(lib.pkv_paged_attention_partitions_list(
+            out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+            block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+            partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_partitions_list")
     return ws
 
 

@@ -254,3 +254,61 @@ def test_prefix_cached_requests_decode_over_shared_blocks():
         v_all = np.concatenate([sys_v, user_kv[s][1]])
         ref = ref_pa.contiguous_attention(q[s], k_all, v_all, 0.088, "bf16")
         assert max_err(got[s], ref) <= GATE["bf16"]
+
+
+@pytest.mark.parametrize("width,part", [(4, 512), (3, 32)])
+def test_beam_search_loop_decodes_every_step(width, part):
+    """P2 §2.2 / P1 §6.2: beam search over 40 steps on a tight pool (finished beams' blocks are
+    handed out again): every step frees the dropped beams, forks the kept ones, appends one
+    token per beam (copy-on-write of shared partial blocks), writes the new K/V and decodes all
+    beams. Device caches stay bit-identical to the oracle's, and every decode matches it."""
+    from workloads import traces
+    P = pk()
+    rng = np.random.default_rng(402700 + width)
+    bs, Hq, H, d, NB, W, dt = 16, 8, 2, 128, 40, 8, "bf16"
+    trace = traces.beam_search_trace(rng, 37, width, 40)
+    order = rng.permutation(NB).astype(np.int32)
+    bm, model = P.BlockManager(NB, bs, order), BlockManagerModel(NB, bs, order)
+    host_k = np.full((NB, H, bs, d), gen.nan_value(dt), dtype=np.uint16)
+    host_v = host_k.copy()
+    kd, vd = to_dev(host_k, dt), to_dev(host_v, dt)
+    bm.add_seq(trace.root, trace.prompt_len)
+    model.add_seq(trace.root, trace.prompt_len)
+    pk_, pv_ = gen.normal(rng, (37, H, d), dt), gen.normal(rng, (37, H, d), dt)
+    slots = bm.slots(trace.root, 0, 37)
+    assert slots.tolist() == model.slots(trace.root, 0, 37)
+    P.reshape_and_cache(to_dev(pk_, dt), to_dev(pv_, dt), kd, vd, i32(slots))
+    host_k, host_v = ref_ops.reshape_and_cache(pk_, pv_, host_k, host_v, slots.tolist())
+    worst = 0.0
+    for step in trace.steps[:-1]:
+        for s in step.frees:
+            bm.free_seq(s)
+            model.free_seq(s)
+        for p_, c_ in step.forks:
+            bm.fork(p_, c_)
+            model.fork(p_, c_)
+        seqs = step.appends
+        sl, pairs = bm.append_slots(seqs)
+        res = [model.append_slot(s) for s in seqs]
+        assert sl.tolist() == [r[1] for r in res]
+        ref_pairs = [[r[2], r[3]] for r in res if r[0] == 1]
+        assert pairs.reshape(-1, 2).tolist() == ref_pairs
+        if ref_pairs:
+            P.copy_blocks(kd, vd, i32(pairs.reshape(-1, 2)))
+            host_k, host_v = ref_ops.copy_blocks(host_k, host_v, ref_pairs)
+        nk, nv = gen.normal(rng, (len(seqs), H, d), dt), gen.normal(rng, (len(seqs), H, d), dt)
+        P.reshape_and_cache(to_dev(nk, dt), to_dev(nv, dt), kd, vd, i32(sl))
+        host_k, host_v = ref_ops.reshape_and_cache(nk, nv, host_k, host_v, sl.tolist())
+        tables, lens = bm.build_tables(seqs, W)
+        for i, s in enumerate(seqs):
+            blocks, n = model.table(s)
+            assert lens[i] == n and tables[i, :len(blocks)].tolist() == blocks
+        q = gen.normal(rng, (len(seqs), Hq, d), dt)
+        case = gen.PagedDecodeCase("beam", dt, Hq, H, d, bs, NB, lens, tables, 0.0884, q=q,
+                                   k_cache=host_k, v_cache=host_v)
+        got, _ = run_decode(case, k=kd, v=vd, partition_size=part)
+        worst = max(worst, max_err(got, oracle(case)))
+        torch.cuda.synchronize()
+        assert _bits_equal(kd, host_k, dt) and _bits_equal(vd, host_v, dt)
+    assert worst <= GATE[dt]
+    assert model.stats()["cow_copies"] > 0

@@ -327,3 +327,63 @@ def test_two_launch_split_matches_oracle():
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     assert max_err(got, oracle(case)) <= GATE["bf16"]
+
+
+# --------------------------------------------------------------------------------------------
+# the per-partition pass over a host work list: bitwise the full-grid result
+# --------------------------------------------------------------------------------------------
+
+def _decode_both(case, part, shuffle=None, extra=None):
+    import paged_kv_cache_402_amd as pk
+    dt = case.dtype
+    B, Hq, D = case.q.shape
+    W = case.block_tables.shape[1]
+    q, k, v = to_dev(case.q, dt), to_dev(case.k_cache, dt), to_dev(case.v_cache, dt)
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    a = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    b = torch.full_like(a, float("nan"))
+    pk.paged_attention_decode(a, q, k, v, tables, lens, case.scale, partition_size=part)
+    items = pk.decode_work_list(case.seq_lens, W, case.block_size, part)
+    if shuffle is not None:
+        items = shuffle.permutation(items)
+    if extra is not None:
+        items = np.concatenate([items, np.asarray(extra, np.int32)])
+    pk.paged_attention_decode(b, q, k, v, tables, lens, case.scale, partition_size=part,
+                              work_list=i32(items))
+    torch.cuda.synchronize()
+    return a.cpu(), b.cpu()
+
+
+@pytest.mark.parametrize("part", [32, 512])
+def test_work_list_decode_is_bitwise_the_grid_decode(part):
+    rng = np.random.default_rng(40)
+    case = gen.make_case("wl", rng, [0, 1, 15, 16, 17, 511, 512, 513, 1024, 1500, 3001], 16, 4,
+                         128, 16, "bf16", width=200)
+    a, b = _decode_both(case, part)
+    assert torch.equal(a, b)
+    assert max_err(b.numpy().astype(np.float64), oracle(case)) <= GATE["bf16"]
+
+
+def test_work_list_order_and_skipped_items():
+    """Any order of the items gives the same bits; items past a sequence's end or naming a
+    sequence beyond the batch do nothing."""
+    rng = np.random.default_rng(41)
+    case = gen.make_case("wl2", rng, [5, 700, 2100, 64], 8, 8, 128, 16, "f16", width=160)
+    junk = [(4 << 16) | 0, (0 << 16) | 3, (1 << 16) | 9]
+    a, b = _decode_both(case, 512, shuffle=np.random.default_rng(3), extra=junk)
+    assert torch.equal(a, b)
+
+
+def test_work_list_full_size_gqa_prefix_bitwise():
+    import paged_kv_cache_402_amd as pk
+    case = gen.llama3_8b_gqa_prefix_case(values=False)
+    q, k, v = _device_values(case, 4021)
+    B, Hq, D = case.num_seqs, case.num_q_heads, case.head_dim
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    a = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    pk.paged_attention_decode(a, q, k, v, tables, lens, case.scale)
+    items = pk.decode_work_list(case.seq_lens, case.table_width, case.block_size, 512)
+    pk.paged_attention_decode(b, q, k, v, tables, lens, case.scale, work_list=i32(items))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
