@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk",
-                   "llama13b_longtail")
+                   "llama13b_longtail", "llama3_8b_long_shared_prefix")
 
 
 def parse_args():
@@ -46,9 +46,11 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
     p.add_argument("--partition", type=int, default=512)
-    p.add_argument("--grid", choices=("list", "full"), default="list",
-                   help="per-partition pass over the host work list (one workgroup per "
-                        "partition that holds tokens) or over the full partition x sequence grid")
+    p.add_argument("--grid", choices=("shared", "list", "full"), default="list",
+                   help="shared: partitions that a group of sequences shares run once for the "
+                        "whole group on the matrix cores, the rest over a work list; list: "
+                        "every partition over the host work list (one workgroup per partition "
+                        "that holds tokens); full: the full partition x sequence grid")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -190,6 +192,20 @@ def host_manager_cost(pk, case, iters=20):
 # ---------------------------------------------------------------------------------------------
 # algorithmic bytes
 # ---------------------------------------------------------------------------------------------
+
+def shared_bytes(case, part, members, pp):
+    """Algorithmic bytes that move from the per-partition kernel to the shared-prefix pass:
+    the shared partitions' KV (read once per KV head), the members' q (read again), the
+    shared partitions' table entries, and the partials of the shared partitions."""
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+    n = int(len(members))
+    kv = case.kv_bytes_per_token() * pp * part
+    tables = 4 * n * pp * (part // case.block_size)
+    partials = n * pp * case.num_q_heads * (case.head_dim + 2) * 4
+    q = n * case.num_q_heads * case.head_dim * eb
+    return {"kv": kv, "tables": tables, "partials": partials, "q": q,
+            "prefix_kernel": kv + 4 * pp * (part // case.block_size) + 4 * n + q + partials}
+
 
 def byte_model(case, part):
     eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
@@ -400,11 +416,20 @@ def main():
     case = st["case"]
     part = args.partition
     bytes_ = byte_model(case, part)
-    work = None
+    work, members, pp = None, None, 0
     if args.grid == "list":
         items = pk.decode_work_list(case.seq_lens, case.table_width, case.block_size, part)
         work = torch.from_numpy(items).to(dev)
         bytes_["decode_kernel"] += 4 * int(items.shape[0])     # one item read per launch
+    elif args.grid == "shared":
+        mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, case.block_size,
+                                               part)
+        work = torch.from_numpy(items).to(dev)
+        members = torch.from_numpy(mem).to(dev)
+        sb = shared_bytes(case, part, mem, pp)
+        bytes_["decode_kernel"] += 4 * int(items.shape[0]) - sb["kv"] - sb["tables"] - sb["partials"]
+        bytes_["prefix_kernel"] = sb["prefix_kernel"]
+        log("shared prefix: %d members, %d partitions" % (mem.shape[0], pp))
     ws = torch.empty(max(1, pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads,
                                                       case.table_width, case.block_size,
                                                       case.head_dim, part)),
@@ -412,7 +437,7 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
 
     def step(i=None):
         if i is not None:
@@ -422,6 +447,11 @@ def main():
         if i is not None:
             ev[i][0].record()
         pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
+        if i is not None:
+            ev[i][5].record()
+        if members is not None and pp > 0:
+            pk.paged_attention_prefix(st["q"], st["k"], st["v"], st["tables"], st["lens"],
+                                      case.scale, members, pp, ws, partition_size=part)
         if i is not None:
             ev[i][1].record()
         # paged_attention_decode's two launches, called apart so each has its own events
@@ -456,7 +486,8 @@ def main():
     ms_wall = (t1 - t0) * 1e3 / K
     # cold: the step's own span between its first and last event (the eviction sits before it)
     ms_step = ms_wall if args.warm else float(np.mean([e[4].elapsed_time(e[3]) for e in ev]))
-    t_cw = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_cw = float(np.mean([e[0].elapsed_time(e[5]) for e in ev]))
+    t_pre = float(np.mean([e[5].elapsed_time(e[1]) for e in ev]))
     t_cb = float(np.mean([e[4].elapsed_time(e[0]) for e in ev]))
     t_dec = [e[1].elapsed_time(e[2]) for e in ev]
     t_red = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
@@ -499,7 +530,8 @@ def main():
         "effective_logical_GBps": round(bytes_["kv_logical"] / (ms_step * 1e-3) / 1e9, 2),
         "kernel_ms": {"decode_partitions": round(dec_ms, 5), "partition_reduce": round(t_red, 5),
                       "copy_blocks": round(t_cb, 5) if st["pairs"] is not None else None,
-                      "reshape_and_cache": round(t_cw, 5)},
+                      "reshape_and_cache": round(t_cw, 5),
+                      "shared_prefix": round(t_pre, 5) if pp > 0 else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(case.name),

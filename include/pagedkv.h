@@ -168,6 +168,61 @@ int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
                                         const int32_t* work_list, int work_items, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Shared-prefix decode (P1 §6.1; P3 §2.2.3, §2.2.8: sequences that start with the same
+ * prompt list the same physical blocks). The leading partitions that a group of sequences
+ * shares are attended once per (KV head, partition) for all the group's query rows, as
+ * matrix-core products, instead of once per sequence; the sequences' own partitions run in
+ * the per-partition pass over a work list that leaves the shared ones out, and the merge pass
+ * combines both. The result equals pkv_paged_attention_decode's up to fp32 rounding (the
+ * shared part sums in another order), not bit for bit.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Host planner, from host copies of the tables and lengths (same layout as the decode
+ * arguments). Candidates are the sequences longer than one partition; they are grouped by
+ * the block ids of their first partition and the largest group is taken (ties: the group
+ * holding the lowest sequence index), if it has at least max(2, min_members) sequences.
+ * prefix_partitions = the number of leading partitions every member lists identically and
+ * that leave every member at least one token after them. members (capacity num_seqs)
+ * receives the group in increasing sequence order, *num_members its size (0 and
+ * *prefix_partitions 0 when no group qualifies). work_list / capacity / return value as in
+ * pkv_decode_work_list, without the members' shared partitions. */
+int pkv_decode_plan_shared_prefix(const int32_t* block_tables, const int32_t* seq_lens,
+                                  int num_seqs, int max_blocks_per_seq, int block_size,
+                                  int partition_size, int min_members, int32_t* members,
+                                  int* num_members, int* prefix_partitions, int32_t* work_list,
+                                  int capacity);
+
+/* All three passes: shared-prefix pass (if num_members and prefix_partitions are > 0), the
+ * per-partition pass over work_list, the merge. members (device int32 [num_members]) and
+ * prefix_partitions come from pkv_decode_plan_shared_prefix, or from a caller that knows
+ * the sharing (the block manager's forks and shared prefixes): every member must list the
+ * first member's block ids in its first prefix_partitions * partition_size / block_size
+ * table entries and be longer than prefix_partitions * partition_size tokens, and work_list
+ * must hold every other partition exactly once. The shared-prefix pass needs fp16 or bf16
+ * KV, head_dim 128 and partition_size / block_size <= 256 (else PKV_EINVAL); the workspace
+ * is the one pkv_decode_workspace_bytes sizes. Members naming a sequence outside the batch
+ * are skipped. */
+int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache, int kv_dtype,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks,
+                                      int max_blocks_per_seq, float scale, int partition_size,
+                                      const int32_t* members, int num_members,
+                                      int prefix_partitions, const int32_t* work_list,
+                                      int work_items, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+/* The shared-prefix pass alone (for timing or scheduling apart): writes the members'
+ * partials of the shared partitions into the workspace. */
+int pkv_paged_attention_prefix(const void* q, const void* k_cache, const void* v_cache,
+                               int kv_dtype, const int32_t* block_tables, const int32_t* seq_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_blocks_per_seq,
+                               float scale, int partition_size, const int32_t* members,
+                               int num_members, int prefix_partitions, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Cache write (P1 §4.3; P3 §2.2.2-§2.2.3): token t's K and V rows ([num_kv_heads][head_dim],
  * contiguous, t-major) are copied bit for bit to slot slot_mapping[t] of k_cache / v_cache.
  * A negative slot skips the token. Slots must be distinct. */

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpagedkv.so")
 
-SOURCES = ["decode.hip", "cache_ops.hip", "capi.cpp", "block_manager.cpp", "pool_plan.cpp"]
+SOURCES = ["decode.hip", "prefix.hip", "cache_ops.hip", "capi.cpp", "block_manager.cpp",
+           "pool_plan.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

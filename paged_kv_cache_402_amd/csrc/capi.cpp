@@ -163,29 +163,38 @@ int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, cons
                     "decode partitions launch");
 }
 
-int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
-                         int block_size, int partition_size, int32_t* work_list, int capacity) {
-  if (partition_size == 0) partition_size = 512;
-  if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "work_list: num_seqs %d out of range", num_seqs);
+}  // extern "C"
+
+namespace {
+
+int check_list_args(const char* who, int num_seqs, int max_blocks_per_seq, int block_size,
+                    int partition_size) {
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "%s: num_seqs %d out of range", who, num_seqs);
   if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
-    return fail(PKV_EINVAL, "work_list: block_size must be a power of two in [8, 256]");
+    return fail(PKV_EINVAL, "%s: block_size must be a power of two in [8, 256]", who);
   if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
-    return fail(PKV_EINVAL, "work_list: max_blocks_per_seq out of range");
+    return fail(PKV_EINVAL, "%s: max_blocks_per_seq out of range", who);
   if (partition_size < 32 || partition_size > 2048 || partition_size % 32 != 0 ||
       partition_size % block_size != 0)
-    return fail(PKV_EINVAL, "work_list: bad partition_size");
-  if (num_seqs > 0 && !seq_lens) return fail(PKV_EINVAL, "work_list: null seq_lens");
+    return fail(PKV_EINVAL, "%s: bad partition_size", who);
   const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
   if ((cap_tokens + partition_size - 1) / partition_size > 65535)
-    return fail(PKV_EINVAL, "work_list: too many partitions per sequence");
-  // full partitions in (sequence, partition) order, then every sequence's last, shorter
-  // partition, longest first (ties in sequence order): the short items end the launch
+    return fail(PKV_EINVAL, "%s: too many partitions per sequence", who);
+  return PKV_OK;
+}
+
+// Items (b << 16 | p) of every partition that holds tokens, except the first skip[b]
+// partitions of sequence b (skip may be null): full partitions in (sequence, partition) order,
+// then the last, shorter partitions longest first, ties in sequence order.
+std::vector<uint32_t> build_work_list(const int32_t* seq_lens, int num_seqs, int64_t cap_tokens,
+                                      int partition_size, const std::vector<int>* skip) {
   std::vector<uint32_t> full;
   std::vector<std::pair<int, uint32_t>> tail;  // (-tokens, item)
   for (int b = 0; b < num_seqs; ++b) {
     const int64_t L = std::min<int64_t>(std::max(seq_lens[b], 0), cap_tokens);
     const int64_t np = L == 0 ? 1 : (L + partition_size - 1) / partition_size;
-    for (int64_t p = 0; p < np; ++p) {
+    const int64_t first = skip ? (*skip)[b] : 0;
+    for (int64_t p = first; p < np; ++p) {
       const int64_t n = std::min<int64_t>(partition_size, L - p * partition_size);
       const uint32_t item = ((uint32_t)b << 16) | (uint32_t)p;
       if (n == partition_size) full.push_back(item);
@@ -196,15 +205,107 @@ int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_p
                    [](const std::pair<int, uint32_t>& x, const std::pair<int, uint32_t>& y) {
                      return x.first < y.first;
                    });
-  const int64_t total = (int64_t)full.size() + (int64_t)tail.size();
-  if (total > INT32_MAX / 8) return fail(PKV_EINVAL, "work_list: too many items");
-  if (work_list == nullptr) return (int)total;     // size query
-  if (capacity < total) return fail(PKV_EINVAL, "work_list: %lld items, capacity %d", (long long)total, capacity);
-  int64_t i = 0;
-  for (uint32_t it : full) work_list[i++] = (int32_t)it;
-  for (const auto& t : tail) work_list[i++] = (int32_t)t.second;
-  ok();
-  return (int)total;
+  for (const auto& t : tail) full.push_back(t.second);
+  return full;
+}
+
+int emit_list(const char* who, const std::vector<uint32_t>& items, int32_t* work_list,
+              int capacity) {
+  if ((int64_t)items.size() > INT32_MAX / 8) return fail(PKV_EINVAL, "%s: too many items", who);
+  const int total = (int)items.size();
+  if (work_list == nullptr) return total;     // size query
+  if (capacity < total) return fail(PKV_EINVAL, "%s: %d items, capacity %d", who, total, capacity);
+  for (int i = 0; i < total; ++i) work_list[i] = (int32_t)items[i];
+  return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
+                         int block_size, int partition_size, int32_t* work_list, int capacity) {
+  if (partition_size == 0) partition_size = 512;
+  int st = check_list_args("work_list", num_seqs, max_blocks_per_seq, block_size, partition_size);
+  if (st != PKV_OK) return st;
+  if (num_seqs > 0 && !seq_lens) return fail(PKV_EINVAL, "work_list: null seq_lens");
+  const auto items = build_work_list(seq_lens, num_seqs, (int64_t)max_blocks_per_seq * block_size,
+                                     partition_size, nullptr);
+  st = emit_list("work_list", items, work_list, capacity);
+  if (st >= 0) ok();
+  return st;
+}
+
+int pkv_decode_plan_shared_prefix(const int32_t* block_tables, const int32_t* seq_lens,
+                                  int num_seqs, int max_blocks_per_seq, int block_size,
+                                  int partition_size, int min_members, int32_t* members,
+                                  int* num_members, int* prefix_partitions, int32_t* work_list,
+                                  int capacity) {
+  if (partition_size == 0) partition_size = 512;
+  int st = check_list_args("plan_shared_prefix", num_seqs, max_blocks_per_seq, block_size,
+                           partition_size);
+  if (st != PKV_OK) return st;
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "plan_shared_prefix: null tables or seq_lens");
+  if (!members || !num_members || !prefix_partitions)
+    return fail(PKV_EINVAL, "plan_shared_prefix: null output");
+  const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int bpp = partition_size / block_size;                 // blocks per partition
+  auto len = [&](int b) { return std::min<int64_t>(std::max(seq_lens[b], 0), cap_tokens); };
+  auto row = [&](int b) { return block_tables + (size_t)b * max_blocks_per_seq; };
+  // candidates: sequences with a full first partition and more tokens after it, grouped by
+  // the block ids of that partition; the largest group wins (ties: lowest first sequence)
+  std::vector<int> order;
+  for (int b = 0; b < num_seqs; ++b)
+    if (len(b) > partition_size) order.push_back(b);
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return std::lexicographical_compare(row(x), row(x) + bpp, row(y), row(y) + bpp);
+  });
+  int best_start = 0, best_n = 0;
+  for (size_t i = 0; i < order.size();) {
+    size_t j = i + 1;
+    while (j < order.size() && std::equal(row(order[i]), row(order[i]) + bpp, row(order[j]))) ++j;
+    const int n = (int)(j - i);
+    const int first = *std::min_element(order.begin() + i, order.begin() + j);
+    const int best_first = best_n ? *std::min_element(order.begin() + best_start,
+                                                      order.begin() + best_start + best_n)
+                                  : INT32_MAX;
+    if (n > best_n || (n == best_n && first < best_first)) {
+      best_start = (int)i;
+      best_n = n;
+    }
+    i = j;
+  }
+  std::vector<int> skip(num_seqs, 0);
+  int pp = 0, nm = 0;
+  if (best_n >= std::max(2, min_members)) {
+    std::vector<int> grp(order.begin() + best_start, order.begin() + best_start + best_n);
+    std::sort(grp.begin(), grp.end());
+    // shared partitions: all members list the first member's blocks, and every member has
+    // tokens after them
+    const int rep = grp[0];
+    pp = (int)((cap_tokens + partition_size - 1) / partition_size);
+    for (int b : grp) {
+      int q = 0;
+      const int64_t max_q = (len(b) - 1) / partition_size;
+      while (q < max_q && q < pp &&
+             std::equal(row(rep) + (size_t)q * bpp, row(rep) + (size_t)(q + 1) * bpp,
+                        row(b) + (size_t)q * bpp))
+        ++q;
+      pp = std::min(pp, q);
+    }
+    for (int b : grp) {
+      members[nm++] = b;
+      skip[b] = pp;
+    }
+  }
+  *num_members = pp > 0 ? nm : 0;
+  *prefix_partitions = pp;
+  const auto items = build_work_list(seq_lens, num_seqs, cap_tokens, partition_size,
+                                     pp > 0 ? &skip : nullptr);
+  st = emit_list("plan_shared_prefix", items, work_list, capacity);
+  if (st >= 0) ok();
+  return st;
 }
 
 static int partitions_list(const DecodePlan& pl0, int kv_dtype, int head_dim,
@@ -250,6 +351,88 @@ int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, con
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
   if (st != PKV_OK || num_seqs == 0) return st;
+  st = partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+static int prefix_pass(const DecodePlan& pl, int kv_dtype, int head_dim, int block_size,
+                       const int32_t* members, int num_members, int prefix_partitions,
+                       void* stream) {
+  if (num_members < 0 || prefix_partitions < 0)
+    return fail(PKV_EINVAL, "prefix: negative member or partition count");
+  if (num_members == 0 || prefix_partitions == 0) return ok();
+  if (!members) return fail(PKV_EINVAL, "prefix: null members");
+  const DecodeArgs& d = pl.args;
+  if (!prefix_supported(kv_dtype, head_dim, pl.group, d.part, d.bs_log2))
+    return fail(PKV_EINVAL, "prefix: needs fp16/bf16 KV, head_dim 128 and at most 256 blocks "
+                "per partition");
+  if ((int64_t)prefix_partitions * d.part > (int64_t)d.max_blocks * block_size ||
+      prefix_partitions >= d.pmax)
+    return fail(PKV_EINVAL, "prefix: %d shared partitions leave no partition of the sequences' "
+                "own", prefix_partitions);
+  const int per = prefix_chunk_seqs(pl.group);
+  if ((int64_t)d.num_kv_heads * ((num_members + per - 1) / per) > INT32_MAX)
+    return fail(PKV_EINVAL, "prefix: too many members");
+  PrefixArgs a;
+  a.q = d.q;
+  a.k_cache = d.k_cache;
+  a.v_cache = d.v_cache;
+  a.block_tables = d.block_tables;
+  a.members = members;
+  a.ws_ml = d.ws_ml;
+  a.ws_acc = d.ws_acc;
+  a.num_members = num_members;
+  a.prefix_parts = prefix_partitions;
+  a.num_seqs = d.num_seqs;
+  a.num_q_heads = d.num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.num_blocks = d.num_blocks;
+  a.max_blocks = d.max_blocks;
+  a.bs_log2 = d.bs_log2;
+  a.part = d.part;
+  a.pmax = d.pmax;
+  a.scale_log2 = d.scale_log2;
+  return hip_status(launch_prefix(a, kv_dtype, pl.group, (hipStream_t)stream),
+                    "shared-prefix launch");
+}
+
+int pkv_paged_attention_prefix(const void* q, const void* k_cache, const void* v_cache,
+                               int kv_dtype, const int32_t* block_tables, const int32_t* seq_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_blocks_per_seq,
+                               float scale, int partition_size, const int32_t* members,
+                               int num_members, int prefix_partitions, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  // out is not written by this pass; q stands in for it in the shared argument checks
+  int st = plan_decode(&pl, const_cast<void*>(q), kv_dtype, q, k_cache, v_cache, kv_dtype,
+                       block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, scale, partition_size,
+                       workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return prefix_pass(pl, kv_dtype, head_dim, block_size, members, num_members, prefix_partitions,
+                     stream);
+}
+
+int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
+                                      const void* k_cache, const void* v_cache, int kv_dtype,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_blocks,
+                                      int max_blocks_per_seq, float scale, int partition_size,
+                                      const int32_t* members, int num_members,
+                                      int prefix_partitions, const int32_t* work_list,
+                                      int work_items, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = prefix_pass(pl, kv_dtype, head_dim, block_size, members, num_members, prefix_partitions,
+                   stream);
+  if (st != PKV_OK) return st;
   st = partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
   if (st != PKV_OK || pl.args.pmax <= 1) return st;
   return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");

@@ -577,7 +577,87 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_
   }
 }
 
+// The same merge with one wave per (sequence, query head), four rows per workgroup, for
+// sequences of a few partitions: D/4 lanes cover a row and 256/D slices of the wave take the
+// partitions in turn; the slices are combined with lane shuffles in a fixed tree (slice 0,
+// which writes the row, always computes the same expression). A quarter of the waves of the
+// 4-wave form, so a batch of short sequences merges in one round of the machine's wave slots.
+template <int D>
+__global__ __launch_bounds__(256) void paged_decode_reduce_rows_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 4;          // lanes per row
+  constexpr int S = 64 / LPR;         // partition slices of the wave
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.num_seqs * a.num_q_heads) return;
+  const int b = row / a.num_q_heads;
+  const int h = row - b * a.num_q_heads;
+  const int cap = a.max_blocks << a.bs_log2;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
+  if (nparts <= 1) return;
+  const int lane = threadIdx.x & 63;
+  const int sl = lane / LPR;
+  const int c = lane % LPR;
+  const size_t base = ((size_t)b * a.num_q_heads + h) * a.pmax;
+  const float* __restrict__ ml = a.ws_ml + base * 2;
+  const float4* __restrict__ acc = reinterpret_cast<const float4*>(a.ws_acc + base * D) + c;
+
+  float m = -INFINITY, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int p = sl; p < nparts; p += S) {
+    const float mp = ml[2 * p];
+    const float lp = ml[2 * p + 1];
+    const float4 x = acc[(size_t)p * LPR];
+    const float mn = fmaxf(m, mp);
+    const float fo = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float fp = mp == -INFINITY ? 0.f : exp2f(mp - mn);
+    den = den * fo + lp * fp;
+    num.x = __builtin_fmaf(x.x, fp, num.x * fo);
+    num.y = __builtin_fmaf(x.y, fp, num.y * fo);
+    num.z = __builtin_fmaf(x.z, fp, num.z * fo);
+    num.w = __builtin_fmaf(x.w, fp, num.w * fo);
+    m = mn;
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    const float mo = __shfl_xor(m, off, 64);
+    const float dn = __shfl_xor(den, off, 64);
+    const float4 no = make_float4(__shfl_xor(num.x, off, 64), __shfl_xor(num.y, off, 64),
+                                  __shfl_xor(num.z, off, 64), __shfl_xor(num.w, off, 64));
+    const float M = fmaxf(m, mo);
+    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
+    den = __builtin_fmaf(f, den, fo * dn);
+    num.x = __builtin_fmaf(f, num.x, fo * no.x);
+    num.y = __builtin_fmaf(f, num.y, fo * no.y);
+    num.z = __builtin_fmaf(f, num.z, fo * no.z);
+    num.w = __builtin_fmaf(f, num.w, fo * no.w);
+    m = M;
+  }
+  if (sl != 0) return;
+  const size_t o = ((size_t)b * a.num_q_heads + h) * D + c * 4;
+  const bool ok = den > 0.f;
+  store_out(a.out, o + 0, ok ? num.x / den : 0.f, a.out_dtype);
+  store_out(a.out, o + 1, ok ? num.y / den : 0.f, a.out_dtype);
+  store_out(a.out, o + 2, ok ? num.z / den : 0.f, a.out_dtype);
+  store_out(a.out, o + 3, ok ? num.w / den : 0.f, a.out_dtype);
+}
+
+// Partitions per sequence up to which the one-wave merge is used.
+constexpr int kRowsReduceMaxParts = 16;
+
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+  if (a.pmax <= kRowsReduceMaxParts) {
+    const dim3 grid((unsigned)(((int64_t)a.num_seqs * a.num_q_heads + 3) / 4));
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<64>, grid, dim3(256), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<128>, grid, dim3(256), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<256>, grid, dim3(256), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(a.num_q_heads, a.num_seqs);
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(paged_decode_reduce_kernel<64>, grid, dim3(256), 0, stream, a); break;

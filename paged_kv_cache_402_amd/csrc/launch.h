@@ -43,6 +43,25 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_
 // Launches the partition merge (grid: Hq x B); only multi-partition sequences do work.
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
+// Shared-prefix pass (prefix.hip): the first prefix_parts partitions of every member
+// sequence list the same physical blocks; one workgroup per (KV head, 64 query rows of the
+// members, partition) writes the members' partials for those partitions.
+struct PrefixArgs {
+  const void* q;               // [B][Hq][D]
+  const void* k_cache;         // [NB][Hkv][bs][D]
+  const void* v_cache;
+  const int32_t* block_tables; // [B][max_blocks]; the first member's row gives the blocks
+  const int32_t* members;      // [num_members] sequence indices
+  float* ws_ml;                // same layout as DecodeArgs
+  float* ws_acc;
+  int num_members, prefix_parts;
+  int num_seqs, num_q_heads, num_kv_heads, num_blocks, max_blocks, bs_log2, part, pmax;
+  float scale_log2;
+};
+bool prefix_supported(int kv_dtype, int head_dim, int group, int part, int bs_log2);
+int prefix_chunk_seqs(int group);   // member sequences per workgroup
+hipError_t launch_prefix(const PrefixArgs& a, int kv_dtype, int group, hipStream_t stream);
+
 struct CacheWriteArgs {
   const void* k;            // [T][Hkv][D]
   const void* v;

@@ -1,0 +1,282 @@
+// Shared-prefix pass of decode attention on gfx950 matrix cores.
+//
+// When many sequences list the same physical blocks for their leading partitions (one
+// system prompt shared by a whole batch: P1 §6.1, P3 §2.2.3 and §2.2.8), the per-sequence
+// pass would read those blocks and redo the same exponentials and products once per
+// sequence. Here one workgroup takes one KV head, one shared partition and 64 query rows of
+// the group at once (16 rows per wave: 16 / G sequences x G query heads), so the products
+// become dense matrix products:
+//   S^T (16 tokens x 16 rows) = K (16 tokens x d) . Q^T (d x 16 rows)     [v_mfma 16x16x32]
+//   O^T (16 cols x 16 rows)  += V^T (16 cols x 32 tokens) . P^T (32 tokens x 16 rows)
+// and it writes the same (max, exponent sum, accumulator) partials as the per-partition
+// kernel, which the partition merge then combines with the sequences' own partitions.
+//
+// Operand layouts of v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies A[l % 16][8g .. 8g+8)
+// and B[8g .. 8g+8)[l % 16], g = l / 16, and receives C[4g + i][l % 16], i = 0..3.
+// With S^T as C, lane l holds the scores of its own row r = l % 16 for the tokens
+// 4g + i and 16 + 4g + i of a 32-token step. The P^T operand of the value product takes those
+// eight values as they lie: the contraction index 8g + e stands for token 4g + e (e < 4) or
+// 16 + 4g + e - 4 (e >= 4), and V^T is read from LDS in that same token order. O^T as C
+// gives lane l its own row's accumulators for columns 16t + 4g + i, so rescaling a row by
+// its new maximum needs no data movement.
+//
+// Softmax weights p are fp32; the value product takes them as two 16-bit operands, p = hi +
+// lo with hi = p rounded and lo = (p - hi) rounded, so the weights keep about 16 significant
+// bits (a single 16-bit p would err by up to 2^-9 relative per weight).
+
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace pkv {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <int DT> __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mma<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// p -> (hi, lo) 16-bit halves with p ~= hi + lo; returns the two 16-bit patterns packed.
+template <int DT> __device__ __forceinline__ void split16(float p, uint32_t& hi, uint32_t& lo);
+template <> __device__ __forceinline__ void split16<BF16>(float p, uint32_t& hi, uint32_t& lo) {
+  hi = narrow_bits<BF16>(p);
+  lo = narrow_bits<BF16>(p - as_f32(hi << 16));
+}
+template <> __device__ __forceinline__ void split16<F16>(float p, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = (_Float16)p;
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, (_Float16)(p - (float)h));
+}
+
+constexpr int kD = 128;                   // head_dim of this pass
+constexpr int kRow = kD * 2;              // bytes of one token row of one head
+constexpr int kVtStride = 32 * 2 + 8;     // bytes of one V^T row in LDS (32 tokens + pad)
+constexpr int kKStride = kRow + 16;       // bytes of one K row in LDS (padded)
+constexpr int kMaxIds = 256;              // block ids of one partition kept in LDS
+
+}  // namespace
+
+// PF: steps of loads in flight ahead of the math; it divides part / 32.
+template <int DT, int G, int PF>
+__global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
+  constexpr int SPW = 16 / G;             // sequences per wave
+  constexpr int SPG = 4 * SPW;            // sequences per workgroup
+  constexpr int NJ = kD / 32;             // d-slices of the score product
+  constexpr int NT = kD / 16;             // column tiles of the value product
+  __shared__ int s_ids[kMaxIds];
+  __shared__ __align__(16) unsigned char s_vt[2][kD * kVtStride];
+  __shared__ __align__(16) unsigned char s_k[2][32 * kKStride];
+
+  const int kvh = blockIdx.x % a.num_kv_heads;
+  const int chunk = blockIdx.x / a.num_kv_heads;
+  const int p = blockIdx.y;                           // shared partition
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+
+  // ---- this lane's query row: member mi, query head h ----
+  // members naming a sequence outside the batch are skipped (their rows read and write
+  // nothing); a first member outside the batch leaves the whole pass without a block list
+  const int rep = a.members[0];
+  if ((unsigned)rep >= (unsigned)a.num_seqs) return;
+  const int mi = chunk * SPG + wave * SPW + r / G;
+  const int bm = mi < a.num_members ? a.members[mi] : -1;
+  const bool valid = (unsigned)bm < (unsigned)a.num_seqs;
+  const int b = valid ? bm : 0;
+  const int h = kvh * G + (r % G);
+  u32x4 qv[NJ];
+  {
+    const unsigned char* qrow =
+        (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + h) * kRow;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qv[j] = valid ? load16(qrow + (32 * j + 8 * g) * 2) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- the partition's block ids (from the first member's table) ----
+  const int nblk = a.part >> a.bs_log2;
+  const int32_t* trow = a.block_tables + (size_t)rep * a.max_blocks +
+                        (((size_t)p * a.part) >> a.bs_log2);
+  for (int i = tid; i < nblk; i += 256) {
+    const int id = trow[i];
+    s_ids[i] = (unsigned)id < (unsigned)a.num_blocks ? id : 0;   // never read outside the pool
+  }
+  __syncthreads();
+
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  const size_t head_bytes = (size_t)kRow << a.bs_log2;       // one (block, head) tile
+  const size_t block_bytes = head_bytes * a.num_kv_heads;
+  const unsigned char* kbase = (const unsigned char*)a.k_cache + kvh * head_bytes;
+  const unsigned char* vbase = (const unsigned char*)a.v_cache + kvh * head_bytes;
+  auto row_off = [&](int tok) -> size_t {                     // partition-relative token
+    const int blk = s_ids[tok >> a.bs_log2];
+    return (size_t)blk * block_bytes + (size_t)(tok & bs_mask) * kRow;
+  };
+
+  // Staging of one 32-token step, shared by the four waves: thread -> token pair tid / 16,
+  // columns 8 (tid % 16) .. +8 of K and of V (four 16-byte loads). K goes to LDS row-major
+  // (rows padded to 272 bytes), V transposed.
+  const int vp = tid >> 4;
+  const int vc = tid & 15;
+  auto load_step = [&](int step, u32x4 (&x)[4]) {
+    const int tok = step * 32 + 2 * vp;
+    const size_t o0 = row_off(tok) + 16 * vc, o1 = row_off(tok + 1) + 16 * vc;
+    x[0] = load16(kbase + o0);
+    x[1] = load16(kbase + o1);
+    x[2] = load16(vbase + o0);
+    x[3] = load16(vbase + o1);
+  };
+  auto store_step = [&](int buf, const u32x4 (&x)[4]) {
+    unsigned char* kd = s_k[buf] + (size_t)(2 * vp) * kKStride + 16 * vc;
+    store16(kd, x[0]);
+    store16(kd + kKStride, x[1]);
+    unsigned char* dst = s_vt[buf] + (size_t)(8 * vc) * kVtStride + 4 * vp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w0 = x[2][e >> 1], w1 = x[3][e >> 1];
+      const uint32_t x0 = (e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
+      const uint32_t x1 = (e & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(dst + e * kVtStride) = x0 | (x1 << 16);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one step of math on the staged tiles of buffer buf
+  auto compute = [&](int buf) {
+    // scores of the 32 tokens for this lane's row (log2 units); K rows 16 hh + r
+    float sc[8];
+    const unsigned char* kt = s_k[buf] + (size_t)r * kKStride + 16 * g;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        c = mma<DT>(load16(kt + (size_t)(16 * hh) * kKStride + 64 * j), qv[j], c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * hh + i] = c[i] * a.scale_log2;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = xor_max_from<16>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    uint32_t ph[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = exp2f(sc[e] - m_new), p1 = exp2f(sc[e + 1] - m_new);
+      psum += p0 + p1;
+      uint32_t h0, l0, h1, l1;
+      split16<DT>(p0, h0, l0);
+      split16<DT>(p1, h1, l1);
+      ph[e >> 1] = h0 | (h1 << 16);
+      pl[e >> 1] = l0 | (l1 << 16);
+    }
+    l_run = l_run * alpha + psum;
+    const u32x4 bhi = u32x4{ph[0], ph[1], ph[2], ph[3]};
+    const u32x4 blo = u32x4{pl[0], pl[1], pl[2], pl[3]};
+    // value product: V^T rows 16 t + r, tokens 4 g .. 4 g + 3 and 16 + 4 g .. + 3
+    const unsigned char* vt = s_vt[buf] + (size_t)r * kVtStride + 8 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const unsigned char* row = vt + (size_t)(16 * t) * kVtStride;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(row + 32);
+      const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
+      f32x4 c = acc[t] * alpha;
+      c = mma<DT>(av, bhi, c);
+      acc[t] = mma<DT>(av, blo, c);
+    }
+  };
+
+  // Loads run kPf steps ahead of the math through a ring of registers; the LDS tiles are
+  // double-buffered, one barrier per step (a buffer is refilled two steps after its reads,
+  // and every wave has passed the barrier in between).
+  // PF divides the step count, so the loop body has no branch: the compiler counts the loads
+  // in flight exactly and waits only for the oldest step's. Past the last step the loads
+  // fetch the last step again.
+  const int steps = a.part >> 5;
+  u32x4 ring[PF][4];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) load_step(min(u, steps - 1), ring[u]);
+  for (int s0 = 0; s0 < steps; s0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int s = s0 + u;
+      store_step(s & 1, ring[u]);
+      load_step(min(s + PF, steps - 1), ring[u]);
+      __syncthreads();
+      compute(s & 1);
+    }
+  }
+
+  const float l_row = xor_sum_from<16>(l_run);
+  if (!valid) return;
+  const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + p;
+  float* dst = a.ws_acc + slot * kD + 4 * g;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    *reinterpret_cast<float4*>(dst + 16 * t) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  if (g == 0) {
+    a.ws_ml[slot * 2] = m_run;
+    a.ws_ml[slot * 2 + 1] = l_row;
+  }
+}
+
+bool prefix_supported(int kv_dtype, int head_dim, int group, int part, int bs_log2) {
+  return (kv_dtype == BF16 || kv_dtype == F16) && head_dim == kD &&
+         (group == 1 || group == 2 || group == 4 || group == 8) && part % 32 == 0 &&
+         (part >> bs_log2) <= kMaxIds;
+}
+
+int prefix_chunk_seqs(int group) { return 4 * (16 / group); }
+
+template <int DT, int G>
+static void launch_pf(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
+  const int steps = a.part >> 5;
+  if (steps % 4 == 0)
+    hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 4>), grid, dim3(256), 0, stream, a);
+  else if (steps % 2 == 0)
+    hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 2>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 1>), grid, dim3(256), 0, stream, a);
+}
+
+template <int DT>
+static hipError_t launch_g(const PrefixArgs& a, int group, hipStream_t stream) {
+  const int per = prefix_chunk_seqs(group);
+  const dim3 grid((unsigned)a.num_kv_heads * ((a.num_members + per - 1) / per),
+                  (unsigned)a.prefix_parts);
+  switch (group) {
+    case 1: launch_pf<DT, 1>(a, grid, stream); break;
+    case 2: launch_pf<DT, 2>(a, grid, stream); break;
+    case 4: launch_pf<DT, 4>(a, grid, stream); break;
+    default: launch_pf<DT, 8>(a, grid, stream); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix(const PrefixArgs& a, int kv_dtype, int group, hipStream_t stream) {
+  return kv_dtype == BF16 ? launch_g<BF16>(a, group, stream) : launch_g<F16>(a, group, stream);
+}
+
+}  // namespace pkv

@@ -64,6 +64,28 @@ def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
     return items
 
 
+def plan_shared_prefix(block_tables, seq_lens, block_size: int,
+                       partition_size: int = DEFAULT_PARTITION, min_members: int = 2):
+    """Host planner of the shared-prefix decode (pkv_decode_plan_shared_prefix) from host
+    tables [B][W] and lengths [B]. Returns (members int32 [n], prefix_partitions, work list
+    int32 without the members' shared partitions); n = prefix_partitions = 0 when no group of
+    at least min_members sequences shares a first partition."""
+    tab = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B, W = tab.shape
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    members = np.zeros(max(1, B), dtype=np.int32)
+    nm, pp = ctypes.c_int(0), ctypes.c_int(0)
+    args = (tab.ctypes.data_as(P_i32), lens.ctypes.data_as(P_i32), B, W, block_size,
+            partition_size, min_members, members.ctypes.data_as(P_i32), ctypes.byref(nm),
+            ctypes.byref(pp))
+    n = check(lib.pkv_decode_plan_shared_prefix(*args, None, 0), "plan_shared_prefix")
+    items = np.empty(n, dtype=np.int32)
+    check(lib.pkv_decode_plan_shared_prefix(*args, items.ctypes.data_as(P_i32), n),
+          "plan_shared_prefix")
+    return members[:nm.value].copy(), pp.value, items
+
+
 def _work(work_list):
     if work_list is None:
         return None, 0
@@ -106,15 +128,29 @@ def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
                            partition_size: int = DEFAULT_PARTITION, workspace=None,
-                           work_list=None):
+                           work_list=None, shared_prefix=None):
     """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
     b's block table locates in the paged caches. With work_list (device int32 from
-    decode_work_list) the per-partition pass runs over that list. Returns `out`."""
+    decode_work_list) the per-partition pass runs over that list. With shared_prefix =
+    (members device int32, prefix_partitions) and the matching work_list (both from
+    plan_shared_prefix) the members' shared partitions run in the shared-prefix pass.
+    Returns `out`."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
     ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
     wsp = ws.data_ptr() if ws is not None else None
-    if work_list is None:
+    if shared_prefix is not None:
+        if work_list is None:
+            raise ValueError("shared_prefix needs the work list plan_shared_prefix returns")
+        mem, pp = shared_prefix
+        _i32(mem, "members")
+        wl, wn = _work(work_list)
+        check(lib.pkv_paged_attention_decode_shared(
+            out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+            block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+            partition_size, mem.data_ptr(), mem.shape[0], int(pp), wl, wn, wsp, wsb, _stream(q)),
+            "paged_attention_decode_shared")
+    elif work_list is None:
         check(lib.pkv_paged_attention_decode(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
@@ -149,6 +185,26 @@ def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
             partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_partitions_list")
     return ws
+
+
+def paged_attention_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, members,
+                           prefix_partitions: int, workspace,
+                           partition_size: int = DEFAULT_PARTITION):
+    """The shared-prefix pass alone: writes the members' partials of the shared partitions
+    into `workspace` (as sized by decode_workspace_bytes)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (workspace, "workspace")):
+        _dev(t, n)
+    _i32(block_tables, "block_tables")
+    _i32(seq_lens, "seq_lens")
+    _i32(members, "members")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    check(lib.pkv_paged_attention_prefix(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), _kv_dtype(k_cache, "k_cache"),
+        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB,
+        block_tables.shape[1], float(scale), partition_size, members.data_ptr(),
+        members.shape[0], int(prefix_partitions), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(q)), "paged_attention_prefix")
 
 
 def paged_attention_reduce(out, seq_lens, block_size, max_blocks_per_seq, workspace,

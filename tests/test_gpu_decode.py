@@ -387,3 +387,92 @@ def test_work_list_full_size_gqa_prefix_bitwise():
     pk.paged_attention_decode(b, q, k, v, tables, lens, case.scale, work_list=i32(items))
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --------------------------------------------------------------------------------------------
+# shared-prefix decode: the members' shared partitions on the matrix cores
+# --------------------------------------------------------------------------------------------
+
+def _share_case(name, seed, lens, hq, hkv, bs, dtype, share_tokens, members, width=None):
+    """A batch whose members list member 0's blocks for their first share_tokens tokens."""
+    rng = np.random.default_rng(seed)
+    case = gen.make_case(name, rng, lens, hq, hkv, 128, bs, dtype, width=width, values=False)
+    nsh = share_tokens // bs
+    for b in members[1:]:
+        case.block_tables[b, :nsh] = case.block_tables[members[0], :nsh]
+    case.q = gen.normal(rng, (len(lens), hq, 128), dtype)
+    case.k_cache, case.v_cache = gen.fill_pool(rng, case.num_blocks, hkv, bs, 128, dtype,
+                                               case.block_tables, case.seq_lens)
+    return case
+
+
+def _run_shared(case, part, min_members=2, members_override=None):
+    import paged_kv_cache_402_amd as pk
+    dt = case.dtype
+    B, Hq, D = case.q.shape
+    W = case.block_tables.shape[1]
+    mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, case.block_size,
+                                           part, min_members)
+    if members_override is not None:
+        mem = np.asarray(members_override, np.int32)
+    q, k, v = to_dev(case.q, dt), to_dev(case.k_cache, dt), to_dev(case.v_cache, dt)
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode(out, q, k, v, tables, lens, case.scale, partition_size=part,
+                              work_list=i32(items), shared_prefix=(i32(mem), pp))
+    plain = torch.full_like(out, float("nan"))
+    pk.paged_attention_decode(plain, q, k, v, tables, lens, case.scale, partition_size=part)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy().astype(np.float64), plain.cpu().numpy().astype(np.float64), mem,
+            pp)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,bs,part,share,n", [
+    ("bf16", 32, 8, 16, 512, 1024, 21),      # G 4: two shared partitions, a partial chunk
+    ("f16", 64, 8, 32, 256, 768, 11),        # G 8: chunks of 8 sequences
+    ("bf16", 8, 8, 8, 128, 384, 40),         # G 1: one partial chunk of 64
+    ("bf16", 16, 8, 64, 64, 256, 9),         # G 2: four one-block partitions
+])
+def test_shared_prefix_decode_matches_oracle(dtype, hq, hkv, bs, part, share, n):
+    rng = np.random.default_rng(50)
+    lens = [int(x) for x in rng.integers(share + 1, share + 2500, size=n)]
+    lens += [300, share + 7]                  # two sequences outside the group
+    members = list(range(n))
+    case = _share_case("shared", 51, lens, hq, hkv, bs, dtype, share, members, width=None)
+    got, plain, mem, pp = _run_shared(case, part)
+    assert mem.tolist() == members and pp == share // part
+    ref = oracle(case)
+    assert np.isfinite(got).all()
+    assert max_err(got, ref) <= GATE[dtype]
+    assert max_err(got, plain) <= 1e-4
+
+
+def test_shared_prefix_full_size_gqa_prefix_sampled():
+    import paged_kv_cache_402_amd as pk
+    case = gen.llama3_8b_gqa_prefix_case(values=False)
+    q, k, v = _device_values(case, 4022)
+    B, Hq, D = case.num_seqs, case.num_q_heads, case.head_dim
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, case.block_size, 512)
+    assert mem.size == B and pp == 1
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode(out, q, k, v, tables, lens, case.scale, work_list=i32(items),
+                              shared_prefix=(i32(mem), pp))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    seqs = sorted(set(np.random.default_rng(2).choice(B, 6, replace=False).tolist())
+                  | {int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))})
+    ref = _sampled_reference(case, q, k, v, seqs)
+    for r, s in enumerate(seqs):
+        assert max_err(got[s], ref[r]) <= GATE["bf16"], "seq %d" % s
+
+
+def test_shared_prefix_members_outside_the_batch_are_skipped():
+    """A member index past the batch reads and writes nothing; the real members still get
+    their shared partitions."""
+    members = list(range(6))
+    case = _share_case("skip", 52, [900] * 6 + [40], 32, 8, 16, "bf16", 512, members)
+    got, plain, mem, pp = _run_shared(case, 512, members_override=members + [7, 1000])
+    assert pp == 1
+    assert max_err(got, oracle(case)) <= GATE["bf16"]

@@ -55,3 +55,51 @@ def test_work_list_sizes_and_errors():
     assert _lib.lib.pkv_decode_work_list(lp, 4, 200, 16, 48, None, 0) == -1     # partition
     assert _lib.lib.pkv_decode_work_list(None, 4, 200, 16, 512, None, 0) == -1
     assert _lib.lib.pkv_decode_work_list(None, 0, 200, 16, 512, None, 0) == 0
+
+
+def _shared_tables(rng, lens, width, bs, share_blocks, members):
+    """Random private tables, then the first share_blocks entries of every member replaced by
+    member 0's (the planner reads nothing but these arrays)."""
+    tab = np.full((len(lens), width), -1, np.int32)
+    ids = rng.permutation(sum(-(-int(L) // bs) for L in lens)).astype(np.int32)
+    nxt = 0
+    for b, L in enumerate(lens):
+        nb = -(-int(L) // bs)
+        tab[b, :nb] = ids[nxt:nxt + nb]
+        nxt += nb
+    for b in members[1:]:
+        tab[b, :share_blocks] = tab[members[0], :share_blocks]
+    return tab
+
+
+def test_plan_shared_prefix_finds_the_group():
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(9)
+    bs, part, W = 16, 512, 300
+    lens = np.array([3000, 600, 1600, 2049, 512, 4000, 1025, 700], np.int32)
+    members = [0, 2, 3, 5, 6]                     # 1 and 7 private, 4 too short to share
+    tab = _shared_tables(rng, lens, W, bs, 64, members)   # 2 full partitions shared
+    tab[4, :32] = tab[0, :32]                     # exactly one partition long: not a candidate
+    mem, pp, items = pk.plan_shared_prefix(tab, lens, bs, part)
+    assert mem.tolist() == members
+    # member 6 has 1025 tokens: only 2 partitions leave it a token of its own
+    assert pp == 2
+    skip = {b: pp for b in members}
+    full = expected(lens, W, bs, part)
+    assert decode(items) == [(b, p) for b, p in full if p >= skip.get(b, 0)]
+
+
+def test_plan_shared_prefix_limits_and_no_group():
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(10)
+    bs, part, W = 16, 256, 200
+    lens = np.array([1000, 1000, 1000, 300], np.int32)
+    tab = _shared_tables(rng, lens, W, bs, 40, [0, 1, 2])   # 2.5 partitions shared
+    mem, pp, items = pk.plan_shared_prefix(tab, lens, bs, part)
+    assert mem.tolist() == [0, 1, 2] and pp == 2
+    mem, pp, items = pk.plan_shared_prefix(tab, lens, bs, part, min_members=4)
+    assert mem.tolist() == [] and pp == 0
+    assert decode(items) == expected(lens, W, bs, part)
+    priv = _shared_tables(rng, lens, W, bs, 0, [0])
+    mem, pp, _ = pk.plan_shared_prefix(priv, lens, bs, part)
+    assert pp == 0 and mem.size == 0

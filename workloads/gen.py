@@ -348,8 +348,20 @@ def long_context_splitk_case(num_seqs: int = 16, values: bool = True, poison: bo
                      width=max_len // 64, fragmented=True, values=values, poison=poison)
 
 
+def llama3_8b_long_shared_prefix_case(num_seqs: int = 256, values: bool = True,
+                                      poison: bool = True) -> PagedDecodeCase:
+    """The GQA 8B shape with a long shared context (a 4096-token document every request
+    reads, as in retrieval over one document: P1 §8.3) and short private suffixes, uniform on
+    [64, 512]. Same seed and layout rules as llama3_8b_gqa_prefix_case."""
+    case = llama3_8b_gqa_prefix_case(num_seqs, values, poison, prefix_tokens=4096,
+                                     max_suffix=512)
+    case.name = "llama3_8b_long_shared_prefix_b%d_bf16" % num_seqs
+    return case
+
+
 WORKLOADS = {
     "tiny": tiny_case,
+    "llama3_8b_long_shared_prefix": llama3_8b_long_shared_prefix_case,
     "llama2_7b_mha": llama2_7b_mha_case,
     "llama3_8b_gqa_prefix": llama3_8b_gqa_prefix_case,
     "llama13b_longtail": llama13b_longtail_case,
