@@ -333,6 +333,50 @@ int pkv_bm_add_seq_cached(pkv_bm* bm, int64_t seq, const int32_t* token_ids, int
 int pkv_bm_prefix_stats(const pkv_bm* bm, int64_t out[4]);
 
 /* ------------------------------------------------------------------------------------------
+ * Continuous batching (P1 §8.2; P3 §2.2.12): a host scheduler over a block manager. Each step
+ * frees the requests that are done, admits waiting requests first come, first served (while
+ * the batch has room, the step's token budget covers their prompt and the pool keeps
+ * watermark_blocks free after taking prompt + 1 tokens; it stops at the first that does not
+ * fit), then gives every running request one token slot in admission order. When the pool is
+ * empty the most recently admitted running request is preempted (P3 §2.2.2, §2.2.5): its
+ * blocks are freed, the tokens it produced join its prompt for recomputation, and it returns
+ * to the front of the queue. Host memory only; one thread per handle; the scheduler owns the
+ * sequences it creates in the manager (sequence id = request id).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct pkv_sched pkv_sched;
+
+/* Step results, in caller-owned arrays: batch, finished, admitted and preempted hold
+ * max_num_seqs ids each, cow_pairs max_num_seqs rows of (src, dst); slots, slot_seq and
+ * slot_pos hold max_step_tokens entries. slots lists the admitted prompts' tokens (request
+ * order, positions 0..prompt-1) and then one token per batch entry; slot_seq / slot_pos name
+ * the request and the token position each slot is for. */
+typedef struct {
+  int64_t* batch;
+  int32_t* slots;
+  int64_t* slot_seq;
+  int32_t* slot_pos;
+  int32_t* cow_pairs;
+  int64_t* finished;
+  int64_t* admitted;
+  int64_t* preempted;
+  int num_batch, num_slots, num_cow, num_finished, num_admitted, num_preempted;
+} pkv_sched_step_out;
+
+/* block_size must be the manager's; max_step_tokens >= max_num_seqs. NULL on bad input. */
+pkv_sched* pkv_sched_create(pkv_bm* bm, int block_size, int max_num_seqs, int max_step_tokens,
+                            int watermark_blocks);
+void pkv_sched_destroy(pkv_sched* s);
+/* Queues a request of prompt_tokens (>= 1) that produces output_tokens (>= 1). prompt +
+ * output must fit max_step_tokens and the pool less the watermark (a preempted request comes
+ * back as one prompt); request ids must be new. */
+int pkv_sched_add_request(pkv_sched* s, int64_t req_id, int prompt_tokens, int output_tokens);
+/* Advances one decode step and fills *out. */
+int pkv_sched_step(pkv_sched* s, pkv_sched_step_out* out);
+/* out[0] waiting, [1] running, [2] finished, [3] admitted, [4] preempted (totals), [5] steps,
+ * [6] decode tokens, [7] prompt tokens written. */
+int pkv_sched_stats(const pkv_sched* s, int64_t out[8]);
+
+/* ------------------------------------------------------------------------------------------
  * KV-pool sizing (P3 §2.2.5, §2.2.7). The pool is fixed at start-up from a memory fraction;
  * this host-only helper turns the device memory, the weights and the model's KV shape into
  * the num_blocks to pass to pkv_bm_create and to allocate the caches with, and into how many

@@ -14,8 +14,10 @@ Modules:
   cache_ops           reference cache write (slot mapping) and whole-block copy
   block_manager_model reference model of the block manager (free list, refcounts, COW, fork)
   pool_plan           KV-pool sizing from the memory fraction, weights and per-token KV bytes
+  scheduler_model     continuous batching: admission, one token per step, preemption
 
 Every function is pinned by tests under tests/ (test_oracle*.py) against values the pages
 print, closed forms, brute force at 50 digits, and an independent library routine.
 """
-from . import storage, paged_attention, cache_ops, block_manager_model, pool_plan  # noqa: F401
+from . import (storage, paged_attention, cache_ops, block_manager_model, pool_plan,  # noqa: F401
+               scheduler_model)

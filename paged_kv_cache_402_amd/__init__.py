@@ -9,6 +9,7 @@ library has not been built (python paged_kv_cache_402_amd/build.py).
 """
 from ._lib import PagedKVError, lib, last_error  # noqa: F401  (raises if the library is missing)
 from .block_manager import BlockManager  # noqa: F401
+from .scheduler import Scheduler  # noqa: F401
 from .pool_plan import kv_pool_plan  # noqa: F401
 from .ops import (copy_blocks, decode_work_list, decode_workspace_bytes,  # noqa: F401
                   paged_attention_decode, paged_attention_partitions, paged_attention_prefix,

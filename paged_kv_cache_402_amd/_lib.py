@@ -70,6 +70,11 @@ SIGNATURES = {
     "pkv_bm_stats": (c_int, [c_void_p, P_i64]),
     "pkv_bm_add_seq_cached": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),
     "pkv_bm_prefix_stats": (c_int, [c_void_p, P_i64]),
+    "pkv_sched_create": (c_void_p, [c_void_p, c_int, c_int, c_int, c_int]),
+    "pkv_sched_destroy": (None, [c_void_p]),
+    "pkv_sched_add_request": (c_int, [c_void_p, c_int64, c_int, c_int]),
+    "pkv_sched_step": (c_int, [c_void_p, c_void_p]),
+    "pkv_sched_stats": (c_int, [c_void_p, P_i64]),
     "pkv_kv_pool_plan": (c_int, [c_int64, c_int64, c_int64, ctypes.c_int32, c_int, c_int, c_int,
                                  c_int, c_int, c_int, c_int, c_int, P_i64]),
 }
