@@ -312,3 +312,55 @@ def test_beam_search_loop_decodes_every_step(width, part):
         assert _bits_equal(kd, host_k, dt) and _bits_equal(vd, host_v, dt)
     assert worst <= GATE[dt]
     assert model.stats()["cow_copies"] > 0
+
+
+def test_continuous_batching_loop_decodes_every_step():
+    """P1 §8.2 / P3 §2.2.12: requests arrive, are admitted, write their prompt, decode one token
+    per step, finish or get preempted (a tight pool) and are recomputed; every step the C++
+    scheduler agrees with the reference model, the device caches stay bit-identical to the
+    oracle's, and every decode matches the oracle's attention."""
+    from oracle.scheduler_model import SchedulerModel
+    from workloads import traces
+    P = pk()
+    rng = np.random.default_rng(402800)
+    bs, Hq, H, d, NB, W, dt = 16, 8, 2, 128, 16, 12, "bf16"
+    reqs = traces.request_stream(rng, 24, 1.5, (1, 80), 10, 40)
+    # K/V of every (request, position): a recomputed token gets the same values again
+    kv = {r.req_id: (gen.normal(rng, (r.prompt_len + r.output_len, H, d), dt),
+                     gen.normal(rng, (r.prompt_len + r.output_len, H, d), dt)) for r in reqs}
+    order = rng.permutation(NB).astype(np.int32)
+    bm, model_bm = P.BlockManager(NB, bs, order), BlockManagerModel(NB, bs, order)
+    sched, model = P.Scheduler(bm, 6, 256, 1), SchedulerModel(model_bm, 6, 256, 1)
+    host_k = np.full((NB, H, bs, d), gen.nan_value(dt), dtype=np.uint16)
+    host_v = host_k.copy()
+    kd, vd = to_dev(host_k, dt), to_dev(host_v, dt)
+    pending = sorted(reqs, key=lambda r: r.arrival)
+    worst, steps, preempted = 0.0, 0, 0
+    while (pending or sched.stats()["waiting"] or sched.stats()["running"]) and steps < 400:
+        while pending and pending[0].arrival <= steps:
+            r = pending.pop(0)
+            sched.add_request(r.req_id, r.prompt_len, r.output_len)
+            model.add_request(r.req_id, r.prompt_len, r.output_len)
+        st, ref = sched.step(), model.step()
+        assert st.batch.tolist() == ref["batch"] and st.slots.tolist() == ref["slots"]
+        preempted += len(st.preempted)
+        if st.cow_pairs.shape[0]:
+            P.copy_blocks(kd, vd, i32(st.cow_pairs))
+            host_k, host_v = ref_ops.copy_blocks(host_k, host_v, st.cow_pairs.tolist())
+        if st.slots.shape[0]:
+            nk = np.stack([kv[s][0][p] for s, p in zip(st.slot_seq.tolist(), st.slot_pos.tolist())])
+            nv = np.stack([kv[s][1][p] for s, p in zip(st.slot_seq.tolist(), st.slot_pos.tolist())])
+            P.reshape_and_cache(to_dev(nk, dt), to_dev(nv, dt), kd, vd, i32(st.slots))
+            host_k, host_v = ref_ops.reshape_and_cache(nk, nv, host_k, host_v, st.slots.tolist())
+        if st.batch.shape[0]:
+            tables, lens = bm.build_tables(st.batch, W)
+            q = gen.normal(rng, (st.batch.shape[0], Hq, d), dt)
+            case = gen.PagedDecodeCase("serve", dt, Hq, H, d, bs, NB, lens, tables, 0.0884, q=q,
+                                       k_cache=host_k, v_cache=host_v)
+            got, _ = run_decode(case, k=kd, v=vd, partition_size=64)
+            worst = max(worst, max_err(got, oracle(case)))
+        steps += 1
+    torch.cuda.synchronize()
+    assert _bits_equal(kd, host_k, dt) and _bits_equal(vd, host_v, dt)
+    assert worst <= GATE[dt]
+    assert sched.stats()["finished"] == len(reqs) and preempted > 0
