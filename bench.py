@@ -45,12 +45,16 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
-    p.add_argument("--partition", type=int, default=512)
+    p.add_argument("--partition", type=int, default=0,
+                   help="tokens per context partition (0: the library's default for the shapes)")
     p.add_argument("--grid", choices=("shared", "list", "full"), default="list",
                    help="shared: partitions that a group of sequences shares run once for the "
                         "whole group on the matrix cores, the rest over a work list; list: "
                         "every partition over the host work list (one workgroup per partition "
                         "that holds tokens); full: the full partition x sequence grid")
+    p.add_argument("--append", choices=("fused", "separate"), default="fused",
+                   help="fused: the decode pass stores the new tokens' K/V itself; separate: "
+                        "reshape_and_cache runs first as its own launch")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -354,7 +358,8 @@ def serve_loop(pk, torch, dev, steps, static=False, warm_steps=None):
     has finished (static batching, P1 §8.2). Returns per-step records of the timed steps."""
     from workloads import traces
     NB, bs, Hq, Hkv, D, W = 10240, 16, 32, 8, 128, 96
-    max_seqs, budget, part = 256, 16384, 512
+    max_seqs, budget = 256, 16384
+    part = pk.default_partition(max_seqs, Hq, Hkv, D, bs, W)
     rng = np.random.default_rng(402900)
     reqs = traces.request_stream(rng, 4000, 2.5, (64, 1024), 128, 512)
     bm = pk.BlockManager(NB, bs)
@@ -522,7 +527,9 @@ def main():
     log("setting up %s" % args.workload)
     st = build_state(args.workload, pk, gen, torch, dev)
     case = st["case"]
-    part = args.partition
+    part = args.partition or pk.default_partition(case.num_seqs, case.num_q_heads,
+                                                  case.num_kv_heads, case.head_dim,
+                                                  case.block_size, case.table_width)
     bytes_ = byte_model(case, part)
     work, members, pp = None, None, 0
     if args.grid == "list":
@@ -545,33 +552,48 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    # the step's stages in launch order; one event before the first and one after each stage
+    # that runs, so a stage's time is the span between its neighbouring events
+    fused = args.append == "fused" and members is None
+    if fused:
+        # the new rows are stored by the decode pass: 2 * B * Hkv * d * eb more bytes written
+        bytes_["decode_kernel"] += bytes_["cache_write"] // 2
+    stages = (["copy_blocks"] if st["pairs"] is not None else []) + \
+        ([] if fused else ["reshape_and_cache"]) + \
+        (["shared_prefix"] if members is not None and pp > 0 else []) + \
+        ["decode_partitions", "partition_reduce"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(K)]
+
+    def run_stage(name):
+        if name == "copy_blocks":
+            pk.copy_blocks(st["k"], st["v"], st["pairs"])
+        elif name == "reshape_and_cache":
+            pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
+        elif name == "shared_prefix":
+            pk.paged_attention_prefix(st["q"], st["k"], st["v"], st["tables"], st["lens"],
+                                      case.scale, members, pp, ws, partition_size=part)
+        elif name == "decode_partitions" and fused:
+            pk.paged_attention_partitions_append(st["out"], st["q"], st["k_new"], st["v_new"],
+                                                 st["k"], st["v"], st["tables"], st["lens"],
+                                                 case.scale, partition_size=part, workspace=ws,
+                                                 work_list=work)
+        elif name == "decode_partitions":
+            # paged_attention_decode's two launches, called apart so each has its own events
+            pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
+                                          st["lens"], case.scale, partition_size=part,
+                                          workspace=ws, work_list=work)
+        else:
+            pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width,
+                                      ws, partition_size=part)
 
     def step(i=None):
         if i is not None:
-            ev[i][4].record()
-        if st["pairs"] is not None:
-            pk.copy_blocks(st["k"], st["v"], st["pairs"])
-        if i is not None:
             ev[i][0].record()
-        pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
-        if i is not None:
-            ev[i][5].record()
-        if members is not None and pp > 0:
-            pk.paged_attention_prefix(st["q"], st["k"], st["v"], st["tables"], st["lens"],
-                                      case.scale, members, pp, ws, partition_size=part)
-        if i is not None:
-            ev[i][1].record()
-        # paged_attention_decode's two launches, called apart so each has its own events
-        pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
-                                      st["lens"], case.scale, partition_size=part, workspace=ws,
-                                      work_list=work)
-        if i is not None:
-            ev[i][2].record()
-        pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width, ws,
-                                  partition_size=part)
-        if i is not None:
-            ev[i][3].record()
+        for j, name in enumerate(stages):
+            run_stage(name)
+            if i is not None:
+                ev[i][j + 1].record()
 
     log("warmup %d" % W)
     for _ in range(W):
@@ -593,19 +615,22 @@ def main():
     t1 = time.perf_counter()
     ms_wall = (t1 - t0) * 1e3 / K
     # cold: the step's own span between its first and last event (the eviction sits before it)
-    ms_step = ms_wall if args.warm else float(np.mean([e[4].elapsed_time(e[3]) for e in ev]))
-    t_cw = float(np.mean([e[0].elapsed_time(e[5]) for e in ev]))
-    t_pre = float(np.mean([e[5].elapsed_time(e[1]) for e in ev]))
-    t_cb = float(np.mean([e[4].elapsed_time(e[0]) for e in ev]))
-    t_dec = [e[1].elapsed_time(e[2]) for e in ev]
-    t_red = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    ms_step = ms_wall if args.warm else float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
+    per = {name: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, name in enumerate(stages)}
+    stage_ms = {name: round(float(np.mean(per[name])), 5) if name in per else None
+                for name in ("decode_partitions", "partition_reduce", "copy_blocks",
+                             "reshape_and_cache", "shared_prefix")}
+    t_dec = per["decode_partitions"]
+    t_red = stage_ms["partition_reduce"]
+    t_cw = stage_ms["reshape_and_cache"]
     dec_ms = float(np.mean(t_dec))
     gbps = bytes_["kv_unique"] / (ms_step * 1e-3) / 1e9
     kernel_bytes = bytes_["decode_kernel"]
     achieved = kernel_bytes / (dec_ms * 1e-3) / 1e9
-    log("step %.4f ms, decode kernel %.4f ms (p10 %.4f, p90 %.4f), reduce %.4f ms, cache write "
-        "%.4f ms" % (ms_step, dec_ms, np.percentile(t_dec, 10), np.percentile(t_dec, 90), t_red,
-                     t_cw))
+    log("step %.4f ms, decode kernel %.4f ms (p10 %.4f, p90 %.4f); %s"
+        % (ms_step, dec_ms, np.percentile(t_dec, 10), np.percentile(t_dec, 90),
+           ", ".join("%s %.4f ms" % (k, v) for k, v in stage_ms.items()
+                     if v is not None and k != "decode_partitions")))
 
     result = {
         "metric": METRIC,
@@ -628,6 +653,7 @@ def main():
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "kv_dtype": case.dtype, "partition_size": part, "grid": args.grid,
+                   "append": "fused" if fused else "separate",
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),
                    "num_blocks": case.num_blocks, "parallelism": "single GPU"},
@@ -636,10 +662,7 @@ def main():
         "kv_unique_bytes": bytes_["kv_unique"],
         "kv_logical_bytes": bytes_["kv_logical"],
         "effective_logical_GBps": round(bytes_["kv_logical"] / (ms_step * 1e-3) / 1e9, 2),
-        "kernel_ms": {"decode_partitions": round(dec_ms, 5), "partition_reduce": round(t_red, 5),
-                      "copy_blocks": round(t_cb, 5) if st["pairs"] is not None else None,
-                      "reshape_and_cache": round(t_cw, 5),
-                      "shared_prefix": round(t_pre, 5) if pp > 0 else None},
+        "kernel_ms": stage_ms,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(case.name),

@@ -133,6 +133,14 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
                                int max_blocks_per_seq, int partition_size,
                                const void* workspace, size_t workspace_bytes, void* stream);
 
+/* A partition size for these shapes: the longest of 2048, 1024, 512 and 256 tokens whose
+ * workgroup fits the LDS and that still gives at least 1024 workgroups if every sequence
+ * were as long as its table allows (256 otherwise). Longer partitions mean fewer
+ * workgroups, less fixed cost per token and fewer partials to merge; the floor keeps small
+ * batches spread over the machine. Negative on bad arguments. */
+int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq);
+
 /* Work list of the per-partition pass, built on the host from host seq_lens: one item per
  * (sequence b, context partition p) that holds tokens, item = (b << 16) | p as int32 bits
  * (a length-0 sequence has one item, p = 0, that writes its zero row). Lengths are clamped
@@ -167,6 +175,38 @@ int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
                                         int max_blocks_per_seq, float scale, int partition_size,
                                         const int32_t* work_list, int work_items, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/* Decode with the cache write of the step's new tokens fused in (P1 §4.3; P3 §2.2.3: the
+ * newest token's K/V are stored into the block the table gives, then attended to): k_new and
+ * v_new ([num_seqs][num_kv_heads][head_dim] of kv_dtype, device) hold the K and V rows of
+ * token seq_lens[b] - 1 of every sequence b with seq_lens[b] > 0. The per-partition pass
+ * reads that token's rows from k_new / v_new and stores them into k_cache / v_cache at the
+ * slot the block table gives (block table[b][(L-1)/block_size], offset (L-1)%block_size),
+ * so the caches end as pkv_reshape_and_cache with those slots would leave them and the output
+ * is bitwise that of pkv_reshape_and_cache followed by the unfused decode. The slot's block
+ * must be held by sequence b alone (the block manager's append gives that); a table entry
+ * outside the pool skips the store and the token. work_list may be NULL (work_items 0) for
+ * the full grid, or a list from pkv_decode_work_list. */
+int pkv_paged_attention_decode_append(void* out, int out_dtype, const void* q, const void* k_new,
+                                      const void* v_new, void* k_cache, void* v_cache,
+                                      int kv_dtype, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int num_blocks, int max_blocks_per_seq, float scale,
+                                      int partition_size, const int32_t* work_list,
+                                      int work_items, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+/* Its per-partition pass alone (the merge is pkv_paged_attention_reduce). */
+int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* q,
+                                          const void* k_new, const void* v_new, void* k_cache,
+                                          void* v_cache, int kv_dtype,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_dim, int block_size, int num_blocks,
+                                          int max_blocks_per_seq, float scale,
+                                          int partition_size, const int32_t* work_list,
+                                          int work_items, void* workspace,
+                                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Shared-prefix decode (P1 §6.1; P3 §2.2.3, §2.2.8: sequences that start with the same

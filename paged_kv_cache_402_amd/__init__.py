@@ -12,7 +12,10 @@ from .block_manager import BlockManager  # noqa: F401
 from .scheduler import Scheduler  # noqa: F401
 from .pool_plan import kv_pool_plan  # noqa: F401
 from .ops import (copy_blocks, decode_work_list, decode_workspace_bytes,  # noqa: F401
-                  paged_attention_decode, paged_attention_partitions, paged_attention_prefix,
+                  default_partition,
+                  paged_attention_decode, paged_attention_decode_append,
+                  paged_attention_partitions, paged_attention_partitions_append,
+                  paged_attention_prefix,
                   paged_attention_reduce, plan_shared_prefix, reshape_and_cache)
 
 __version__ = "0.1.0"

@@ -29,6 +29,7 @@ SIGNATURES = {
                                                c_void_p, c_size_t, c_void_p]),
     "pkv_paged_attention_reduce": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_decode_default_partition": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "pkv_decode_work_list": (c_int, [P_i32, c_int, c_int, c_int, c_int, P_i32, c_int]),
     "pkv_paged_attention_decode_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                 c_int, c_void_p, c_void_p, c_int, c_int, c_int,
@@ -39,6 +40,17 @@ SIGNATURES = {
                                                     c_int, c_int, c_int, c_int, c_int, c_int,
                                                     c_float, c_int, c_void_p, c_int, c_void_p,
                                                     c_size_t, c_void_p]),
+    "pkv_paged_attention_decode_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                                  c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                                  c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                  c_float, c_int, c_void_p, c_int, c_void_p,
+                                                  c_size_t, c_void_p]),
+    "pkv_paged_attention_partitions_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
+                                                      c_void_p, c_void_p, c_void_p, c_int,
+                                                      c_void_p, c_void_p, c_int, c_int, c_int,
+                                                      c_int, c_int, c_int, c_int, c_float, c_int,
+                                                      c_void_p, c_int, c_void_p, c_size_t,
+                                                      c_void_p]),
     "pkv_decode_plan_shared_prefix": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
                                               P_i32, P_int, P_int, P_i32, c_int]),
     "pkv_paged_attention_decode_shared": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,

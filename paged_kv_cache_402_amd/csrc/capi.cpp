@@ -121,6 +121,8 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.out_dtype = out_dtype;
   a.work = nullptr;
   a.work_items = 0;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   pl->group = group;
   pl->ws_needed = need;
   return ok();
@@ -222,6 +224,28 @@ int emit_list(const char* who, const std::vector<uint32_t>& items, int32_t* work
 }  // namespace
 
 extern "C" {
+
+int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      head_dim <= 0 || !is_pow2(block_size) || block_size < 8 || block_size > 256 ||
+      max_blocks_per_seq <= 0)
+    return fail(PKV_EINVAL, "default_partition: bad argument");
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
+  // the longest partition that fits the LDS and still gives the machine work: at least
+  // kMinGroups workgroups even if every sequence were as long as its table allows
+  constexpr int64_t kMinGroups = 1024;
+  int part = 2048;
+  while (part > 256) {
+    const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((tokens + part - 1) / part);
+    if (decode_lds_bytes(PKV_BF16, head_dim, group, part) <= kMaxDecodeLds && groups >= kMinGroups)
+      break;
+    part /= 2;
+  }
+  ok();
+  return part;
+}
 
 int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
                          int block_size, int partition_size, int32_t* work_list, int capacity) {
@@ -354,6 +378,63 @@ int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, con
   st = partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
   if (st != PKV_OK || pl.args.pmax <= 1) return st;
   return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+static int append_args(DecodePlan* pl, const void* k_new, const void* v_new) {
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "decode_append: null k_new or v_new");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_EINVAL, "decode_append: k_new and v_new must be 16-byte aligned");
+  pl->args.k_new = k_new;
+  pl->args.v_new = v_new;
+  return PKV_OK;
+}
+
+static int partitions_any(const DecodePlan& pl, int kv_dtype, int head_dim,
+                          const int32_t* work_list, int work_items, void* stream) {
+  if (work_list == nullptr && work_items == 0)
+    return hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group,
+                                               (hipStream_t)stream),
+                      "decode partitions launch");
+  return partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
+}
+
+int pkv_paged_attention_decode_append(void* out, int out_dtype, const void* q, const void* k_new,
+                                      const void* v_new, void* k_cache, void* v_cache,
+                                      int kv_dtype, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int num_blocks, int max_blocks_per_seq, float scale,
+                                      int partition_size, const int32_t* work_list,
+                                      int work_items, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  st = partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* q,
+                                          const void* k_new, const void* v_new, void* k_cache,
+                                          void* v_cache, int kv_dtype,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_dim, int block_size, int num_blocks,
+                                          int max_blocks_per_seq, float scale,
+                                          int partition_size, const int32_t* work_list,
+                                          int work_items, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  return partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
 }
 
 static int prefix_pass(const DecodePlan& pl, int kv_dtype, int head_dim, int block_size,

@@ -190,6 +190,27 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     const int j = k * 64 + lane;
     ids[k] = j < nblk ? trow[j] : 0;
   }
+  // ---- appended token (optional): the K and V rows of token L - 1 come from k_new /
+  // v_new instead of the cache, and the workgroup of (KV head, last partition) stores them
+  // into the cache slot the table gives; no other workgroup reads that slot in this launch
+  const bool fused = a.k_new != nullptr;
+  const int last = L - 1 - t0;                       // partition-relative; outside [0, n): none
+  const size_t new_off = ((size_t)b * a.num_kv_heads + kvh) * K::RB;
+  const unsigned char* knew = fused ? (const unsigned char*)a.k_new + new_off : nullptr;
+  const unsigned char* vnew = fused ? (const unsigned char*)a.v_new + new_off : nullptr;
+  if (fused && last >= 0 && last < n && wave == 0) {
+    const int blk = pick_id(ids, last >> a.bs_log2);
+    if ((unsigned)blk < (unsigned)a.num_blocks) {
+      const size_t row = (size_t)blk * block_bytes + (size_t)(last & bs_mask) * K::RB;
+      for (int c = lane; c < 2 * K::C; c += 64) {
+        const bool isv = c >= K::C;
+        const int cc = isv ? c - K::C : c;
+        unsigned char* dst = (unsigned char*)(isv ? a.v_cache : a.k_cache) + kvh * head_bytes + row;
+        store16(dst + cc * 16, load16((isv ? vnew : knew) + cc * 16));
+      }
+    }
+  }
+
   const int kr = lane / K::LK;  // token row inside a K step
   const int kc = lane % K::LK;  // this lane's vectors: kc, kc+LK, ...
   const unsigned char* qsrc =
@@ -234,6 +255,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
           okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
           const unsigned char* p = kbase + (size_t)(okb[u] ? blk : 0) * block_bytes +
                                    (uint32_t)(((tok & bs_mask) + rl) * K::RB + kg * 16);
+          if (fused && tok + rl == last) p = knew + kg * 16;
 #pragma unroll
           for (int j = 0; j < NJ; ++j) kb[u][j] = load16(p + j * 64);
         } else {
@@ -282,6 +304,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
         const unsigned char* p = kbase + (size_t)(okb[u] ? blk : 0) * block_bytes +
                                  (uint32_t)(((tok & bs_mask) + kr) * K::RB + kc * 16);
+        if (fused && tok + kr == last) p = knew + kc * 16;
 #pragma unroll
         for (int i = 0; i < K::NLK; ++i) kv[u][i] = load16(p + i * K::LK * 16);
       } else {
@@ -334,6 +357,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         okv[u] = (unsigned)blk < (unsigned)a.num_blocks;
         const unsigned char* p = vbase + (size_t)(okv[u] ? blk : 0) * block_bytes +
                                  (uint32_t)(((tok & bs_mask) + vr) * K::RB + vc * 16);
+        if (fused && tok + vr == last) p = vnew + vc * 16;
 #pragma unroll
         for (int i = 0; i < K::NLV; ++i) vv[u][i] = load16(p + i * K::LV * 16);
       }

@@ -31,6 +31,10 @@ struct DecodeArgs {
   // null: one workgroup per (KV head, partition, sequence) of the full pmax x B grid.
   const uint32_t* work;
   int work_items;
+  // Optional appended token: [B][Hkv][D] K and V rows of token seq_lens[b] - 1, read from
+  // here instead of the cache and stored into the cache by the pass (null: none).
+  const void* k_new;
+  const void* v_new;
 };
 
 // Bytes of dynamic LDS one decode workgroup needs.

@@ -47,6 +47,23 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: 
                                               block_size, head_dim, partition_size))
 
 
+def default_partition(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      block_size: int, max_blocks_per_seq: int) -> int:
+    """The partition size pkv_decode_default_partition picks for these shapes (2048, 1024, 512
+    or 256 tokens)."""
+    return check(lib.pkv_decode_default_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  block_size, max_blocks_per_seq),
+                 "default_partition")
+
+
+def _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list, shared_prefix=None):
+    if partition_size is not None:
+        return partition_size
+    if work_list is not None or shared_prefix is not None:
+        raise ValueError("pass the partition_size the work list was built with")
+    return default_partition(B, Hq, Hkv, D, bs, W)
+
+
 def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
                      partition_size: int = DEFAULT_PARTITION) -> np.ndarray:
     """Host work list of the per-partition pass (pkv_decode_work_list) from host lengths:
@@ -127,16 +144,19 @@ def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                           partition_size: int = DEFAULT_PARTITION, workspace=None,
-                           work_list=None, shared_prefix=None):
+                           partition_size=None, workspace=None, work_list=None,
+                           shared_prefix=None):
     """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
     b's block table locates in the paged caches. With work_list (device int32 from
     decode_work_list) the per-partition pass runs over that list. With shared_prefix =
     (members device int32, prefix_partitions) and the matching work_list (both from
     plan_shared_prefix) the members' shared partitions run in the shared-prefix pass.
+    partition_size None picks default_partition's (then no work list may be given).
     Returns `out`."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
+    partition_size = _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list,
+                                        shared_prefix)
     ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
     wsp = ws.data_ptr() if ws is not None else None
     if shared_prefix is not None:
@@ -184,6 +204,53 @@ def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
             partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_partitions_list")
+    return ws
+
+
+def _append_args(k_new, v_new, k_cache, B):
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, n)
+        if t.dtype != k_cache.dtype or t.shape != (B, k_cache.shape[1], k_cache.shape[3]):
+            raise ValueError("%s must be [B][Hkv][D] of the cache dtype" % n)
+
+
+def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
+                                  scale, partition_size=None, workspace=None, work_list=None):
+    """Stores every sequence's newest token (k_new / v_new, [B][Hkv][D], token seq_lens[b] - 1)
+    into the caches at the slot its block table gives and decodes, in one pass plus the merge:
+    the same caches and bitwise the same output as reshape_and_cache then
+    paged_attention_decode. Returns `out`."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    partition_size = _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list)
+    _append_args(k_new, v_new, k_cache, B)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_decode_append(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_decode_append")
+    return out
+
+
+def paged_attention_partitions_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                      seq_lens, scale, partition_size: int = DEFAULT_PARTITION,
+                                      workspace=None, work_list=None):
+    """First pass of paged_attention_decode_append only. Returns the workspace for
+    paged_attention_reduce."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    _append_args(k_new, v_new, k_cache, B)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_partitions_append(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_partitions_append")
     return ws
 
 
