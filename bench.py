@@ -545,10 +545,10 @@ def main():
         bytes_["decode_kernel"] += 4 * int(items.shape[0]) - sb["kv"] - sb["tables"] - sb["partials"]
         bytes_["prefix_kernel"] = sb["prefix_kernel"]
         log("shared prefix: %d members, %d partitions" % (mem.shape[0], pp))
-    ws = torch.empty(max(1, pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads,
-                                                      case.table_width, case.block_size,
-                                                      case.head_dim, part)),
-                     dtype=torch.uint8, device=dev)
+    # no workspace: no sequence spans two partitions and the merge pass has nothing to do
+    ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
+                                         case.block_size, case.head_dim, part)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
@@ -561,7 +561,7 @@ def main():
     stages = (["copy_blocks"] if st["pairs"] is not None else []) + \
         ([] if fused else ["reshape_and_cache"]) + \
         (["shared_prefix"] if members is not None and pp > 0 else []) + \
-        ["decode_partitions", "partition_reduce"]
+        ["decode_partitions"] + (["partition_reduce"] if ws_bytes > 0 else [])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(K)]
 
