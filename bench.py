@@ -69,6 +69,9 @@ def parse_args():
                         "(scheduler + cache writes + decode every step) and, on the same "
                         "traffic, static batching")
     p.add_argument("--serve-steps", type=int, default=400)
+    p.add_argument("--prefix-cache", action="store_true",
+                   help="only count how many requests sharing system prompts a pool admits "
+                        "with and without the prefix cache (host block manager, no GPU)")
     p.add_argument("--fork-tree", action="store_true",
                    help="only count the blocks branch trees hold (host block manager, no GPU)")
     return p.parse_args()
@@ -443,6 +446,48 @@ def serve_report(pk, torch, dev, steps):
     print(json.dumps(out), flush=True)
 
 
+def prefix_cache_admission(pk, num_blocks, bs, system_lens, rng, cached, max_requests=100000):
+    """Admits requests (a system prompt drawn uniformly from `system_lens`' prompts, then a
+    private user part of U[16, 512] random token ids) into a fixed pool until one does not
+    fit. Returns (requests admitted, prompt tokens, tokens found in the cache)."""
+    prompts = [rng.integers(0, 32000, n).astype(np.int32) for n in system_lens]
+    bm = pk.BlockManager(num_blocks, bs)
+    admitted = tokens = hit_tokens = 0
+    while admitted < max_requests:
+        sysp = prompts[int(rng.integers(0, len(prompts)))]
+        user = rng.integers(0, 32000, int(rng.integers(16, 513))).astype(np.int32)
+        toks = np.concatenate([sysp, user])
+        if cached:
+            st, hit = bm.add_seq_cached_status(admitted, toks)
+        else:
+            st, hit = bm.add_seq_status(admitted, int(toks.shape[0])), 0
+        if st < 0:
+            break
+        admitted += 1
+        tokens += int(toks.shape[0])
+        hit_tokens += hit
+    bm.close()
+    return admitted, tokens, hit_tokens
+
+
+def prefix_cache_report(pk):
+    """P3 §2.2.8 / §2.2.11: requests that share a system prompt reuse its cached blocks, so a
+    pool of 10240 blocks of 16 tokens admits more of them. Seeded; host only."""
+    rows = []
+    for k in (1, 4, 16):
+        for sys_len in (256, 512, 1024, 2048):
+            res = {}
+            for cached in (False, True):
+                rng = np.random.default_rng(403000 + k * 10000 + sys_len)
+                res[cached] = prefix_cache_admission(pk, 10240, 16, [sys_len] * k, rng, cached)
+            a0, a1 = res[False][0], res[True][0]
+            rows.append({"system_prompts": k, "system_tokens": sys_len, "admitted_private": a0,
+                         "admitted_cached": a1, "capacity_gain": round(a1 / a0 - 1, 4),
+                         "prompt_tokens_cached": round(res[True][2] / res[True][1], 4)})
+    print(json.dumps({"prefix_cache": True, "num_blocks": 10240, "block_size": 16,
+                      "user_tokens": "U[16, 512]", "rows": rows}), flush=True)
+
+
 def fork_tree_report(pk):
     """Blocks held by branch trees on the block manager against private copies per branch
     (every branch holding ceil(tokens / block_size) blocks of its own). Prompts of
@@ -509,9 +554,12 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), flush=True)
         sys.exit(2)
-    if args.fork_tree:
+    if args.fork_tree or args.prefix_cache:
         import paged_kv_cache_402_amd as pk
-        fork_tree_report(pk)
+        if args.fork_tree:
+            fork_tree_report(pk)
+        if args.prefix_cache:
+            prefix_cache_report(pk)
         return
     import torch
     import paged_kv_cache_402_amd as pk
