@@ -587,6 +587,17 @@ def main():
     elif args.grid == "shared":
         mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, case.block_size,
                                                part)
+        # the shared pass launches (KV heads x row chunks x shared partitions) workgroups: with
+        # no partition asked for, halve the partition while that gives under two per compute
+        # unit (512)
+        while not args.partition and part > 256 and pp > 0:
+            chunks = -(-mem.shape[0] // (64 // (case.num_q_heads // case.num_kv_heads)))
+            if case.num_kv_heads * chunks * pp >= 512:
+                break
+            part //= 2
+            bytes_ = byte_model(case, part)
+            mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens,
+                                                   case.block_size, part)
         work = torch.from_numpy(items).to(dev)
         members = torch.from_numpy(mem).to(dev)
         sb = shared_bytes(case, part, mem, pp)

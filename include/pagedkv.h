@@ -134,8 +134,8 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
                                const void* workspace, size_t workspace_bytes, void* stream);
 
 /* A partition size for these shapes: the longest of 2048, 1024, 512 and 256 tokens whose
- * workgroup fits the LDS and that still gives at least 1024 workgroups if every sequence
- * were as long as its table allows (256 otherwise). Longer partitions mean fewer
+ * workgroup takes at most 40 KiB of LDS (four per compute unit) and that still gives at least
+ * 1024 workgroups if every sequence were as long as its table allows (256 otherwise). Longer partitions mean fewer
  * workgroups, less fixed cost per token and fewer partials to merge; the floor keeps small
  * batches spread over the machine. Negative on bad arguments. */
 int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -233,13 +233,15 @@ int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads
     return fail(PKV_EINVAL, "default_partition: bad argument");
   const int group = num_q_heads / num_kv_heads;
   const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-  // the longest partition that fits the LDS and still gives the machine work: at least
-  // kMinGroups workgroups even if every sequence were as long as its table allows
+  // the longest partition whose workgroup leaves room for four per compute unit in the LDS
+  // (160 KiB each) and that still gives the machine work: at least kMinGroups workgroups
+  // even if every sequence were as long as its table allows
   constexpr int64_t kMinGroups = 1024;
+  constexpr size_t kDefaultLds = 40 * 1024;
   int part = 2048;
   while (part > 256) {
     const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((tokens + part - 1) / part);
-    if (decode_lds_bytes(PKV_BF16, head_dim, group, part) <= kMaxDecodeLds && groups >= kMinGroups)
+    if (decode_lds_bytes(PKV_BF16, head_dim, group, part) <= kDefaultLds && groups >= kMinGroups)
       break;
     part /= 2;
   }

@@ -32,7 +32,7 @@
 //   * V pass: LV lanes (16) own one token row; each lane accumulates p * v for its 8 (or 4)
 //     columns and every head of the group in fp32;
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
-//     LDS with their maxima; a sequence that fits one partition gets its output row
+//     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence that fits one partition gets its output row
 //     directly, longer ones leave (max, sum, accumulator) partials that a second kernel
 //     merges (deterministic split-K, no atomics).
 // Tokens past the sequence end, and blocks whose table entry lies outside the pool, are
@@ -167,12 +167,15 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const int c0 = min(n, wave * share);
   const int nw = min(n - c0, share);
 
-  // LDS: per-wave scores [NW][part/NW][G], then the merge area [NW][G][D] and [NW][G] x 2
-  const int wcap = a.part / NW;
-  float* s_sc = reinterpret_cast<float*>(smem) + (size_t)wave * wcap * G;
-  float* s_acc = reinterpret_cast<float*>(smem) + (size_t)a.part * G;
-  float* s_m = s_acc + NW * G * D;
-  float* s_l = s_m + NW * G;
+  // LDS: one area per wave, [part/NW][G] scores; after its V pass the wave's scores are dead
+  // and its merge data ([G][D] accumulator, [G] max, [G] sum) go in their place, so the
+  // workgroup needs no separate merge area (at 2048-token partitions and G = 4 that keeps it
+  // at 32 KiB, five workgroups' worth of a compute unit's 160 KiB instead of three)
+  const int wstride = max(a.part / NW, D + 2) * G;      // floats per wave
+  float* s_sc = reinterpret_cast<float*>(smem) + (size_t)wave * wstride;
+  auto w_acc = [&](int w) { return reinterpret_cast<float*>(smem) + (size_t)w * wstride; };
+  auto w_m = [&](int w) { return w_acc(w) + G * D; };
+  auto w_l = [&](int w) { return w_acc(w) + G * D + G; };
 
   const int bs_mask = (1 << a.bs_log2) - 1;
   const size_t head_bytes = ((size_t)1 << a.bs_log2) * K::RB;   // one (block, head) tile
@@ -422,19 +425,22 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < K::ACC; ++e) acc[g][e] = xor_sum_from<K::LV>(acc[g][e]);
+  // every lane's score reads are done before the area is reused (LDS keeps a wave's order)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
   if (vr == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int i = 0; i < K::NLV; ++i)
-        lds_store_n<K::PER16>(s_acc + (wave * G + g) * D + (i * K::LV + vc) * K::PER16,
+        lds_store_n<K::PER16>(w_acc(wave) + g * D + (i * K::LV + vc) * K::PER16,
                               &acc[g][i * K::PER16]);
   }
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      s_m[wave * G + g] = m[g];
-      s_l[wave * G + g] = l[g];
+      w_m(wave)[g] = m[g];
+      w_l(wave)[g] = l[g];
     }
   }
   __syncthreads();
@@ -444,16 +450,16 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   for (int idx = tid; idx < G * D; idx += NT) {
     const int g = idx / D;
     const int d = idx - g * D;
-    float M = s_m[g];
+    float M = w_m(0)[g];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w * G + g]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, w_m(w)[g]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float mw = s_m[w * G + g];
+      const float mw = w_m(w)[g];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      num = __builtin_fmaf(f, s_acc[(w * G + g) * D + d], num);
-      den = __builtin_fmaf(f, s_l[w * G + g], den);
+      num = __builtin_fmaf(f, w_acc(w)[g * D + d], num);
+      den = __builtin_fmaf(f, w_l(w)[g], den);
     }
     const int h = kvh * G + g;
     if (single) {
@@ -546,8 +552,9 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) 
 
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
   (void)kv_dtype;
-  // per-wave scores (part x group floats in all) + merge area
-  return ((size_t)part * group + (size_t)kDecodeWaves * group * (head_dim + 2)) * 4;
+  // per wave: its scores (part / 4 x group floats), reused for its merge data afterwards
+  const size_t per = (size_t)(part / kDecodeWaves > head_dim + 2 ? part / kDecodeWaves : head_dim + 2);
+  return (size_t)kDecodeWaves * per * group * 4;
 }
 
 template <int DT, int D, int G>

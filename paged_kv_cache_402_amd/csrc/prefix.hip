@@ -126,11 +126,12 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
     return (size_t)blk * block_bytes + (size_t)(tok & bs_mask) * kRow;
   };
 
-  // Staging of one 32-token step, shared by the four waves: thread -> token pair tid / 16,
-  // columns 8 (tid % 16) .. +8 of K and of V (four 16-byte loads). K goes to LDS row-major
-  // (rows padded to 272 bytes), V transposed.
-  const int vp = tid >> 4;
-  const int vc = tid & 15;
+  // Staging of one 32-token step, shared by the four waves: thread -> token pair tid % 16,
+  // columns 8 (tid / 16) .. +8 of K and of V (four 16-byte loads). K goes to LDS row-major
+  // (rows padded to 272 bytes), V transposed; with this mapping the 32 lanes of one LDS cycle
+  // write the transposed V tile to 32 different banks (token pairs 0..15 of two column groups).
+  const int vp = tid & 15;
+  const int vc = tid >> 4;
   auto load_step = [&](int step, u32x4 (&x)[4]) {
     const int tok = step * 32 + 2 * vp;
     const size_t o0 = row_off(tok) + 16 * vc, o1 = row_off(tok + 1) + 16 * vc;
@@ -160,15 +161,32 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
 
   // one step of math on the staged tiles of buffer buf
   auto compute = [&](int buf) {
+    // every LDS operand of the step first (K: 8 x 16 B, V^T: 16 x 8 B), so their latencies
+    // overlap one another and the products instead of being paid one read at a time
+    const unsigned char* kt = s_k[buf] + (size_t)r * kKStride + 16 * g;
+    const unsigned char* vt = s_vt[buf] + (size_t)r * kVtStride + 8 * g;
+    u32x4 ka[2][NJ];
+    u32x4 av[NT];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) ka[hh][j] = load16(kt + (size_t)(16 * hh) * kKStride + 64 * j);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // V^T rows 16 t + r, tokens 4 g .. 4 g + 3 and 16 + 4 g .. + 3
+      const unsigned char* row = vt + (size_t)(16 * t) * kVtStride;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(row + 32);
+      av[t] = u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // scores of the 32 tokens for this lane's row (log2 units); K rows 16 hh + r
     float sc[8];
-    const unsigned char* kt = s_k[buf] + (size_t)r * kKStride + 16 * g;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        c = mma<DT>(load16(kt + (size_t)(16 * hh) * kKStride + 64 * j), qv[j], c);
+      for (int j = 0; j < NJ; ++j) c = mma<DT>(ka[hh][j], qv[j], c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * hh + i] = c[i] * a.scale_log2;
     }
@@ -194,17 +212,11 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
     l_run = l_run * alpha + psum;
     const u32x4 bhi = u32x4{ph[0], ph[1], ph[2], ph[3]};
     const u32x4 blo = u32x4{pl[0], pl[1], pl[2], pl[3]};
-    // value product: V^T rows 16 t + r, tokens 4 g .. 4 g + 3 and 16 + 4 g .. + 3
-    const unsigned char* vt = s_vt[buf] + (size_t)r * kVtStride + 8 * g;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const unsigned char* row = vt + (size_t)(16 * t) * kVtStride;
-      const uint2 x0 = *reinterpret_cast<const uint2*>(row);
-      const uint2 x1 = *reinterpret_cast<const uint2*>(row + 32);
-      const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
       f32x4 c = acc[t] * alpha;
-      c = mma<DT>(av, bhi, c);
-      acc[t] = mma<DT>(av, blo, c);
+      c = mma<DT>(av[t], bhi, c);
+      acc[t] = mma<DT>(av[t], blo, c);
     }
   };
 
@@ -252,10 +264,9 @@ int prefix_chunk_seqs(int group) { return 4 * (16 / group); }
 
 template <int DT, int G>
 static void launch_pf(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
+  // two steps of loads in flight measured best (four hold more registers for no gain)
   const int steps = a.part >> 5;
-  if (steps % 4 == 0)
-    hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 4>), grid, dim3(256), 0, stream, a);
-  else if (steps % 2 == 0)
+  if (steps % 2 == 0)
     hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 2>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((paged_prefix_kernel<DT, G, 1>), grid, dim3(256), 0, stream, a);
