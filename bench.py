@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk",
-                   "llama13b_longtail", "llama3_8b_long_shared_prefix")
+                   "llama13b_longtail", "llama3_8b_long_shared_prefix", "llama3_8b_short_batch")
 
 
 def parse_args():
@@ -55,6 +55,9 @@ def parse_args():
     p.add_argument("--append", choices=("fused", "separate"), default="fused",
                    help="fused: the decode pass stores the new tokens' K/V itself; separate: "
                         "reshape_and_cache runs first as its own launch")
+    p.add_argument("--pack", type=int, default=0,
+                   help="with --grid list: partitions of at most this many tokens run four to a "
+                        "workgroup, one wave each (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -580,7 +583,13 @@ def main():
                                                   case.block_size, case.table_width)
     bytes_ = byte_model(case, part)
     work, members, pp = None, None, 0
-    if args.grid == "list":
+    if args.grid == "list" and args.pack > 0:
+        items, rows = pk.decode_work_list_packed(case.seq_lens, case.table_width,
+                                                 case.block_size, part, args.pack)
+        work = (torch.from_numpy(items).to(dev), rows)
+        bytes_["decode_kernel"] += 4 * int(items.shape[0])     # rows and packed items
+        log("work list: %d rows, %d entries" % (rows, items.shape[0]))
+    elif args.grid == "list":
         items = pk.decode_work_list(case.seq_lens, case.table_width, case.block_size, part)
         work = torch.from_numpy(items).to(dev)
         bytes_["decode_kernel"] += 4 * int(items.shape[0])     # one item read per launch
@@ -712,6 +721,7 @@ def main():
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "kv_dtype": case.dtype, "partition_size": part, "grid": args.grid,
+                   "pack_tokens": args.pack if args.grid == "list" else 0,
                    "append": "fused" if fused else "separate",
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),

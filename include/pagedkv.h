@@ -146,19 +146,36 @@ int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads
  * (a length-0 sequence has one item, p = 0, that writes its zero row). Lengths are clamped
  * to [0, max_blocks_per_seq * block_size] as the kernel clamps them. Order: the full
  * partitions in (sequence, partition) order, then every sequence's last, shorter partition,
- * longest first. With work_list NULL returns the item count; otherwise writes the items
- * (capacity >= count, else PKV_EINVAL) and returns the count. Negative on bad arguments. */
+ * longest first. num_seqs is at most 32767 (an item's top bit stays clear). With work_list
+ * NULL returns the item count; otherwise writes the items (capacity >= count, else
+ * PKV_EINVAL) and returns the count. Negative on bad arguments. */
 int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
                          int block_size, int partition_size, int32_t* work_list, int capacity);
 
+/* The same list with its short partitions packed: items of at most pack_tokens tokens
+ * (0 < pack_tokens <= partition_size / 4; 0 packs nothing) are taken four at a time by one
+ * workgroup, one wave each, for the same KV head, instead of one workgroup each. A serving
+ * mix of many short sequences then needs a quarter of the workgroups for them; each is latency
+ * bound (a chain of dependent loads), so the launch shortens. Layout: *rows entries first,
+ * each a plain item or a packed row 0x80000000 | idx naming the four items stored at
+ * idx .. idx + 3 further on in the list (a last, partial group is padded with items naming
+ * sequence 0xFFFF, which every launch skips). Pass the whole list and work_items = *rows to
+ * the _list and _append entry points. A packed wave computes its partition alone, so those
+ * outputs equal the four-wave ones up to fp32 rounding order, not bitwise. Returns the list
+ * length (with work_list NULL: a size query, *rows still set); negative on bad arguments. */
+int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
+                                int block_size, int partition_size, int pack_tokens,
+                                int32_t* work_list, int capacity, int* rows);
+
 /* pkv_paged_attention_decode / _partitions with the per-partition pass launched over a work
- * list (device int32 [work_items], from pkv_decode_work_list) instead of the full
- * (partition, sequence) grid: one workgroup per (KV head, item), so no workgroup is spent on
- * partitions past a sequence's end, and the short last partitions run at the end of the
- * launch. The list must hold every partition of every sequence exactly once (the merge pass
- * reads all of them); items naming a sequence >= num_seqs or a partition past the
- * sequence's end are skipped. Every partition computes exactly what it computes in the
- * full-grid launch, so the output is bitwise the same. */
+ * list (device int32, from pkv_decode_work_list, or pkv_decode_work_list_packed with
+ * work_items its rows) instead of the full (partition, sequence) grid: one workgroup per
+ * (KV head, row), so no workgroup is spent on partitions past a sequence's end, and the short
+ * last partitions run at the end of the launch. num_seqs is at most 32767. The list must hold
+ * every partition of every sequence exactly once (the merge pass reads all of them); items
+ * naming a sequence >= num_seqs or a partition past the sequence's end are skipped. Every
+ * partition of a plain list computes exactly what it computes in the full-grid launch, so the
+ * output is bitwise the same. */
 int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, const void* k_cache,
                                     const void* v_cache, int kv_dtype,
                                     const int32_t* block_tables, const int32_t* seq_lens,

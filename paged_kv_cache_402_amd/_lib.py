@@ -31,6 +31,8 @@ SIGNATURES = {
                                            c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "pkv_decode_default_partition": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "pkv_decode_work_list": (c_int, [P_i32, c_int, c_int, c_int, c_int, P_i32, c_int]),
+    "pkv_decode_work_list_packed": (c_int, [P_i32, c_int, c_int, c_int, c_int, c_int, P_i32,
+                                            c_int, P_int]),
     "pkv_paged_attention_decode_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                 c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                 c_int, c_int, c_int, c_int, c_float, c_int,

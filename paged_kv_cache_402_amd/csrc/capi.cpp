@@ -35,6 +35,7 @@ int ok() {
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxListSeqs = 32767;      // work-list items keep their top bit clear
 constexpr size_t kMaxDecodeLds = 64 * 1024;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -171,7 +172,8 @@ namespace {
 
 int check_list_args(const char* who, int num_seqs, int max_blocks_per_seq, int block_size,
                     int partition_size) {
-  if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "%s: num_seqs %d out of range", who, num_seqs);
+  if (num_seqs < 0 || num_seqs > kMaxListSeqs)
+    return fail(PKV_EINVAL, "%s: num_seqs %d out of range [0, %d]", who, num_seqs, kMaxListSeqs);
   if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
     return fail(PKV_EINVAL, "%s: block_size must be a power of two in [8, 256]", who);
   if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
@@ -209,6 +211,30 @@ std::vector<uint32_t> build_work_list(const int32_t* seq_lens, int num_seqs, int
                    });
   for (const auto& t : tail) full.push_back(t.second);
   return full;
+}
+
+// Rows of a packed list: the items of more than pack_tokens tokens as they are, then one
+// row (kPackedRow | idx) per four consecutive shorter items, which are stored after the rows
+// from index idx (the last group padded with items naming sequence 0xFFFF, which every
+// launch skips). items are in build_work_list order, so the short ones are its tail.
+std::vector<uint32_t> pack_work_list(const std::vector<uint32_t>& items, const int32_t* seq_lens,
+                                     int64_t cap_tokens, int partition_size, int pack_tokens,
+                                     int* rows) {
+  auto tokens = [&](uint32_t it) {
+    const int64_t L = std::min<int64_t>(std::max(seq_lens[it >> 16], 0), cap_tokens);
+    return std::min<int64_t>(partition_size, L - (int64_t)(it & 0xFFFFu) * partition_size);
+  };
+  size_t first = items.size();
+  while (first > 0 && tokens(items[first - 1]) <= pack_tokens) --first;
+  const size_t nshort = items.size() - first;
+  const size_t groups = (nshort + 3) / 4;
+  std::vector<uint32_t> out(items.begin(), items.begin() + (long)first);
+  const size_t base = first + groups;
+  for (size_t g = 0; g < groups; ++g) out.push_back(kPackedRow | (uint32_t)(base + 4 * g));
+  *rows = (int)out.size();
+  for (size_t i = 0; i < 4 * groups; ++i)
+    out.push_back(i < nshort ? items[first + i] : 0xFFFF0000u);
+  return out;
 }
 
 int emit_list(const char* who, const std::vector<uint32_t>& items, int32_t* work_list,
@@ -259,6 +285,34 @@ int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_p
                                      partition_size, nullptr);
   st = emit_list("work_list", items, work_list, capacity);
   if (st >= 0) ok();
+  return st;
+}
+
+int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
+                                int block_size, int partition_size, int pack_tokens,
+                                int32_t* work_list, int capacity, int* rows) {
+  if (partition_size == 0) partition_size = 512;
+  int st = check_list_args("work_list_packed", num_seqs, max_blocks_per_seq, block_size,
+                           partition_size);
+  if (st != PKV_OK) return st;
+  if (num_seqs > 0 && !seq_lens) return fail(PKV_EINVAL, "work_list_packed: null seq_lens");
+  if (!rows) return fail(PKV_EINVAL, "work_list_packed: null rows");
+  if (pack_tokens < 0 || pack_tokens > partition_size / kDecodeWaves)
+    return fail(PKV_EINVAL, "work_list_packed: pack_tokens %d outside [0, partition_size / 4]",
+                pack_tokens);
+  const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const auto items = build_work_list(seq_lens, num_seqs, cap_tokens, partition_size, nullptr);
+  int r = (int)items.size();
+  const auto list = pack_tokens > 0
+                        ? pack_work_list(items, seq_lens, cap_tokens, partition_size, pack_tokens, &r)
+                        : items;
+  if ((int64_t)list.size() > (int64_t)(kPackedRow - 1))
+    return fail(PKV_EINVAL, "work_list_packed: too many items");
+  st = emit_list("work_list_packed", list, work_list, capacity);
+  if (st >= 0) {
+    *rows = r;
+    ok();
+  }
   return st;
 }
 
@@ -339,6 +393,9 @@ static int partitions_list(const DecodePlan& pl0, int kv_dtype, int head_dim,
   if (work_items < 0) return fail(PKV_EINVAL, "decode: negative work_items");
   if (work_items == 0) return ok();
   if (!work_list) return fail(PKV_EINVAL, "decode: null work_list");
+  // an item's top bit marks a packed row, so listed sequences stay below 32768
+  if (pl0.args.num_seqs > kMaxListSeqs)
+    return fail(PKV_EINVAL, "decode: a work list takes at most %d sequences", kMaxListSeqs);
   if ((int64_t)work_items * pl0.args.num_kv_heads > INT32_MAX)
     return fail(PKV_EINVAL, "decode: work list too long");
   DecodePlan pl = pl0;

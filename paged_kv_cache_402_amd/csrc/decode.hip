@@ -19,7 +19,9 @@
 //     running first;
 //   * each wave owns a quarter of the partition and works through it on its own: no
 //     workgroup barrier until the final merge, so the four waves never wait for each other
-//     and their loads stay in flight independently;
+//     and their loads stay in flight independently. A packed row of the work list instead
+//     gives each wave a short partition of its own (four items, one KV head), with no merge:
+//     a batch of short sequences then needs a quarter of the workgroups;
 //   * the partition's physical block ids are loaded once, one per lane, before any KV load;
 //     a step's id is then read with v_readlane, so no KV load waits on a table lookup;
 //   * K pass: LK lanes (8, or 16 for rows of more than 256 bytes) own one token row; each
@@ -133,13 +135,24 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   constexpr int NT = kDecodeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
 
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
   int kvh, pi, b;
+  // packed row: the four waves take four short partitions (four items stored from index
+  // idx of the list) of the same KV head, each on its own, with no merge between them
+  bool packed = false;
   if (a.work != nullptr) {
-    // consecutive workgroups take the KV heads of one item, so with 8 KV heads each XCD of
+    // consecutive workgroups take the KV heads of one row, so with 8 KV heads each XCD of
     // the round-robin dispatch keeps to one head
     const unsigned item = blockIdx.x / (unsigned)a.num_kv_heads;
     kvh = blockIdx.x - item * a.num_kv_heads;
-    const uint32_t w = a.work[item];
+    uint32_t w = a.work[item];
+    if (w & kPackedRow) {
+      packed = true;
+      w = a.work[(w & ~kPackedRow) + wave];
+    }
     b = (int)(w >> 16);
     pi = (int)(w & 0xFFFFu);
     if (b >= a.num_seqs) return;
@@ -155,17 +168,17 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   if (pi >= nparts) return;
   const int t0 = pi * a.part;                  // a multiple of the block size
   const int n = max(0, min(L - t0, a.part));   // tokens of this partition
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // a packed wave's partition must fit its LDS area (the list builder packs at most
+  // part / 4 tokens); a list that breaks this leaves the item unwritten
+  if (packed && n > a.part / NW) return;
 
   // this wave's share of the partition: [c0, c0 + nw), partition-relative; a multiple of
-  // every step size (the matrix-core K pass takes 16 tokens per step)
+  // every step size (the matrix-core K pass takes 16 tokens per step). A packed wave takes
+  // its whole partition.
   constexpr int STEP = MF && K::STEP < 16 ? 16 : K::STEP;
   const int share = (((n + NW - 1) / NW) + STEP - 1) / STEP * STEP;
-  const int c0 = min(n, wave * share);
-  const int nw = min(n - c0, share);
+  const int c0 = packed ? 0 : min(n, wave * share);
+  const int nw = packed ? n : min(n - c0, share);
 
   // LDS: one area per wave, [part/NW][G] scores; after its V pass the wave's scores are dead
   // and its merge data ([G][D] accumulator, [G] max, [G] sum) go in their place, so the
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const size_t new_off = ((size_t)b * a.num_kv_heads + kvh) * K::RB;
   const unsigned char* knew = fused ? (const unsigned char*)a.k_new + new_off : nullptr;
   const unsigned char* vnew = fused ? (const unsigned char*)a.v_new + new_off : nullptr;
-  if (fused && last >= 0 && last < n && wave == 0) {
+  if (fused && last >= 0 && last < n && (packed || wave == 0)) {
     const int blk = pick_id(ids, last >> a.bs_log2);
     if ((unsigned)blk < (unsigned)a.num_blocks) {
       const size_t row = (size_t)blk * block_bytes + (size_t)(last & bs_mask) * K::RB;
@@ -425,6 +438,37 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < K::ACC; ++e) acc[g][e] = xor_sum_from<K::LV>(acc[g][e]);
+
+  const bool single = nparts == 1;
+  if (packed) {
+    // the merge of one wave: f = 1 (0 when nothing was readable), out = acc / l
+    if (vr == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float f = m[g] == -INFINITY ? 0.f : 1.f;
+        const float den = __builtin_fmaf(f, l[g], 0.f);
+        const int h = kvh * G + g;
+        const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + pi;
+#pragma unroll
+        for (int i = 0; i < K::NLV; ++i)
+#pragma unroll
+          for (int e = 0; e < K::PER16; ++e) {
+            const int d = (i * K::LV + vc) * K::PER16 + e;
+            const float num = __builtin_fmaf(f, acc[g][i * K::PER16 + e], 0.f);
+            if (single)
+              store_out(a.out, ((size_t)b * a.num_q_heads + h) * D + d,
+                        den > 0.f ? num / den : 0.f, a.out_dtype);
+            else
+              a.ws_acc[slot * D + d] = num;
+          }
+        if (!single && vc == 0) {
+          a.ws_ml[slot * 2] = m[g];
+          a.ws_ml[slot * 2 + 1] = den;
+        }
+      }
+    }
+    return;
+  }
   // every lane's score reads are done before the area is reused (LDS keeps a wave's order)
   __builtin_amdgcn_wave_barrier();
   asm volatile("" ::: "memory");
@@ -446,7 +490,6 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   __syncthreads();
 
   // ---- merge the waves; write the output row or this partition's partials ----
-  const bool single = nparts == 1;
   for (int idx = tid; idx < G * D; idx += NT) {
     const int g = idx / D;
     const int d = idx - g * D;

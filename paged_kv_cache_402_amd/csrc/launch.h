@@ -11,6 +11,9 @@ namespace pkv {
 // Workgroup shape of the decode kernel: 4 waves of 64 lanes.
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = 4;
+// Work-list row flag: the row (flag | idx) stands for the four items stored at idx .. idx + 3
+// of the list, one per wave of the workgroup.
+constexpr uint32_t kPackedRow = 0x80000000u;
 
 struct DecodeArgs {
   void* out;                   // [B][Hq][D] of out dtype

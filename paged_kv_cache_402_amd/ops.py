@@ -81,6 +81,26 @@ def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
     return items
 
 
+def decode_work_list_packed(seq_lens, max_blocks_per_seq: int, block_size: int,
+                            partition_size: int = DEFAULT_PARTITION, pack_tokens: int = 64):
+    """Host work list with the partitions of at most pack_tokens tokens packed four to a
+    workgroup (pkv_decode_work_list_packed). Returns (list int32, rows): upload the list and
+    pass work_list=(tensor, rows)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    lp = lens.ctypes.data_as(P_i32)
+    rows = ctypes.c_int(0)
+    n = check(lib.pkv_decode_work_list_packed(lp, lens.shape[0], max_blocks_per_seq, block_size,
+                                              partition_size, pack_tokens, None, 0,
+                                              ctypes.byref(rows)), "decode_work_list_packed")
+    items = np.empty(n, dtype=np.int32)
+    check(lib.pkv_decode_work_list_packed(lp, lens.shape[0], max_blocks_per_seq, block_size,
+                                          partition_size, pack_tokens,
+                                          items.ctypes.data_as(P_i32), n, ctypes.byref(rows)),
+          "decode_work_list_packed")
+    return items, rows.value
+
+
 def plan_shared_prefix(block_tables, seq_lens, block_size: int,
                        partition_size: int = DEFAULT_PARTITION, min_members: int = 2):
     """Host planner of the shared-prefix decode (pkv_decode_plan_shared_prefix) from host
@@ -104,12 +124,20 @@ def plan_shared_prefix(block_tables, seq_lens, block_size: int,
 
 
 def _work(work_list):
+    """A device list, or (device list, rows) for a packed list: pointer and row count."""
     if work_list is None:
         return None, 0
+    rows = None
+    if isinstance(work_list, tuple):
+        work_list, rows = work_list
     _i32(work_list, "work_list")
     if work_list.dim() != 1:
         raise ValueError("work_list must be 1-D")
-    return work_list.data_ptr(), work_list.shape[0]
+    if rows is None:
+        rows = work_list.shape[0]
+    elif not 0 <= int(rows) <= work_list.shape[0]:
+        raise ValueError("work_list rows %d outside [0, %d]" % (rows, work_list.shape[0]))
+    return work_list.data_ptr(), int(rows)
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens):
@@ -148,7 +176,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
                            shared_prefix=None):
     """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
     b's block table locates in the paged caches. With work_list (device int32 from
-    decode_work_list) the per-partition pass runs over that list. With shared_prefix =
+    decode_work_list, or (device list, rows) from decode_work_list_packed) the per-partition
+    pass runs over that list. With shared_prefix =
     (members device int32, prefix_partitions) and the matching work_list (both from
     plan_shared_prefix) the members' shared partitions run in the shared-prefix pass.
     partition_size None picks default_partition's (then no work list may be given).

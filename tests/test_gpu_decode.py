@@ -391,6 +391,152 @@ def test_work_list_full_size_gqa_prefix_bitwise():
 
 
 # --------------------------------------------------------------------------------------------
+# packed work lists: short partitions four to a workgroup, one wave each
+# --------------------------------------------------------------------------------------------
+
+def _packed_rows_items(lst, rows):
+    u = np.asarray(lst, np.int32).view(np.uint32)
+    packed = set()
+    for r in u[:rows]:
+        if r & 0x80000000:
+            i = int(r & 0x7FFFFFFF)
+            packed |= {(int(x >> 16), int(x & 0xFFFF)) for x in u[i:i + 4]}
+    return packed
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,part,pack", [
+    ("bf16", 32, 32, 128, 16, 2048, 64),      # MHA, the long-tail serving shape
+    ("f16", 40, 40, 128, 32, 2048, 512),      # every partition of <= 512 tokens packed
+    ("bf16", 32, 8, 128, 16, 512, 128),       # G 4
+    ("bf16", 64, 8, 128, 64, 1024, 64),       # G 8: matrix-core score product
+    ("f32", 8, 4, 64, 8, 128, 32),
+    ("bf16", 8, 2, 256, 16, 256, 64),
+])
+def test_packed_work_list_matches_oracle(dtype, hq, hkv, d, bs, part, pack):
+    """Partitions of at most `pack` tokens run one wave each; the rest as in the plain list.
+    Lengths cover empty sequences, single tokens, short sequences (packed, single partition),
+    sequences whose short last partition is packed and merged with full ones (partials), a
+    last group padded to four, and a row of NaN-poisoned slots past every end."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(70)
+    lens = [0, 1, 2, 5, bs - 1, bs, pack, pack + 1, part, part + 1, part + pack, 2 * part + 3,
+            3 * part, 700, 33, 17, 9]
+    case = gen.make_case("pk", rng, lens, hq, hkv, d, bs, dtype, width=-(-max(lens) // bs) + 2)
+    B, W = len(lens), case.block_tables.shape[1]
+    q, k, v = to_dev(case.q, dtype), to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    tables, lns = i32(case.block_tables), i32(case.seq_lens)
+    lst, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, part, pack)
+    assert rows < len(lst)                      # something was packed
+    a = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    b = torch.full_like(a, float("nan"))
+    pk.paged_attention_decode(a, q, k, v, tables, lns, case.scale, partition_size=part,
+                              work_list=i32(pk.decode_work_list(case.seq_lens, W, bs, part)))
+    pk.paged_attention_decode(b, q, k, v, tables, lns, case.scale, partition_size=part,
+                              work_list=(i32(lst), rows))
+    torch.cuda.synchronize()
+    got = b.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert max_err(got, oracle(case)) <= GATE[dtype]
+    # sequences none of whose partitions was packed are bitwise the plain list's
+    packed = _packed_rows_items(lst, rows)
+    for s, L in enumerate(lens):
+        if not any(it[0] == s for it in packed):
+            assert torch.equal(a[s], b[s]), s
+
+
+def test_packed_work_list_fused_append():
+    """The packed wave of a sequence's last partition stores the appended token: caches are
+    bitwise those of reshape_and_cache + decode, outputs within the gate of the oracle."""
+    import paged_kv_cache_402_amd as pk
+    dtype, hq, hkv, d, bs, part, pack = "f16", 16, 16, 128, 32, 1024, 128
+    rng = np.random.default_rng(71)
+    lens = [1, 2, 31, 32, 33, 100, 1024, 1030, 2100, 64, 0]
+    case = gen.make_case("pkapp", rng, lens, hq, hkv, d, bs, dtype, width=2100 // bs + 2)
+    B, W = len(lens), case.block_tables.shape[1]
+    k_new, v_new = gen.normal(rng, (B, hkv, d), dtype), gen.normal(rng, (B, hkv, d), dtype)
+    slots = np.array([-1 if L == 0 else
+                      int(case.block_tables[b, (L - 1) // bs]) * bs + (L - 1) % bs
+                      for b, L in enumerate(lens)], np.int32)
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    for sl in slots:
+        if sl >= 0:
+            kc[sl // bs, :, sl % bs, :] = gen.nan_value(dtype)
+            vc[sl // bs, :, sl % bs, :] = gen.nan_value(dtype)
+    q, tables, lns = to_dev(case.q, dtype), i32(case.block_tables), i32(case.seq_lens)
+    lst, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, part, pack)
+    k1, v1 = to_dev(kc, dtype), to_dev(vc, dtype)
+    pk.reshape_and_cache(to_dev(k_new, dtype), to_dev(v_new, dtype), k1, v1, i32(slots))
+    k2, v2 = to_dev(kc, dtype), to_dev(vc, dtype)
+    out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode_append(out, q, to_dev(k_new, dtype), to_dev(v_new, dtype), k2, v2,
+                                     tables, lns, case.scale, partition_size=part,
+                                     work_list=(i32(lst), rows))
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    ref = gen.PagedDecodeCase("pkapp", dtype, hq, hkv, d, bs, case.num_blocks, case.seq_lens,
+                              case.block_tables, case.scale, q=case.q,
+                              k_cache=to_host(k2, dtype), v_cache=to_host(v2, dtype))
+    assert max_err(out.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
+
+
+def test_packed_work_list_long_tail_full_size_sampled():
+    """The long-tail serving shape at full size (128 sequences, 40 MHA heads, fp16, block 32,
+    geometric lengths of mean 200 clipped to [1, 2048]) with 2048-token partitions and
+    partitions of at most 64 tokens packed, in the fp16 output the benchmark writes, against
+    the oracle on sampled sequences (the shortest, the longest and random ones)."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(72)
+    lens = np.clip(rng.geometric(1.0 / 200, size=128), 1, 2048).astype(np.int32)
+    case = gen.make_case("pklt", rng, lens, 40, 40, 128, 32, "f16", width=64, values=False)
+    q, k, v = _device_values(case, 4023)
+    lst, rows = pk.decode_work_list_packed(case.seq_lens, 64, 32, 2048, 64)
+    assert rows < len(lst)
+    out = torch.full((128, 40, 128), float("nan"), dtype=torch.float16, device="cuda")
+    pk.paged_attention_decode(out, q, k, v, i32(case.block_tables), i32(case.seq_lens),
+                              case.scale, partition_size=2048, work_list=(i32(lst), rows))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    order = np.argsort(lens, kind="stable")
+    seqs = sorted(set(order[:6].tolist()) | set(order[-3:].tolist())
+                  | {int(x) for x in rng.choice(128, 5, replace=False)})
+    ref = _sampled_reference(case, q, k, v, seqs)
+    for r, s_ in enumerate(seqs):
+        gate = GATE["f16"] + half_ulp(ref[r], "f16")
+        assert (np.abs(got[s_] - ref[r]) <= gate).all(), "seq %d" % s_
+
+
+def test_packed_work_list_short_batch_full_size_sampled():
+    """2048 short GQA sequences (lengths 1..48), every partition packed (32 and 48 tokens),
+    against the oracle on sampled sequences and against the plain list."""
+    import paged_kv_cache_402_amd as pk
+    case = gen.llama3_8b_short_batch_case(values=False)
+    q, k, v = _device_values(case, 4024)
+    B, W, bs = case.num_seqs, case.table_width, case.block_size
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    plain = torch.empty((B, 32, 128), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode(plain, q, k, v, tables, lens, case.scale, partition_size=2048,
+                              work_list=i32(pk.decode_work_list(case.seq_lens, W, bs, 2048)))
+    rng = np.random.default_rng(5)
+    seqs = sorted(set(rng.choice(B, 8, replace=False).tolist())
+                  | {int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))})
+    ref = _sampled_reference(case, q, k, v, seqs)
+    for pack in (32, 48):
+        lst, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, 2048, pack)
+        out = torch.full_like(plain, float("nan"))
+        pk.paged_attention_decode(out, q, k, v, tables, lens, case.scale, partition_size=2048,
+                                  work_list=(i32(lst), rows))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        for r, s_ in enumerate(seqs):
+            assert max_err(got[s_], ref[r]) <= GATE["bf16"], "seq %d pack %d" % (s_, pack)
+        # the same attention up to fp32 rounding order
+        assert float((out - plain).abs().max()) <= 1e-5
+
+
+# --------------------------------------------------------------------------------------------
 # shared-prefix decode: the members' shared partitions on the matrix cores
 # --------------------------------------------------------------------------------------------
 

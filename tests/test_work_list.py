@@ -57,6 +57,77 @@ def test_work_list_sizes_and_errors():
     assert _lib.lib.pkv_decode_work_list(None, 0, 200, 16, 512, None, 0) == 0
 
 
+def unpack(lst, rows):
+    """Rows of a packed list as lists of (b, p) items: a plain row is one item, a packed row
+    (top bit set) the four items stored at its index."""
+    u = np.asarray(lst, dtype=np.int32).view(np.uint32)
+    out = []
+    for r in u[:rows]:
+        if r & 0x80000000:
+            i = int(r & 0x7FFFFFFF)
+            assert rows <= i and i + 4 <= len(u)
+            out.append([(int(x >> 16), int(x & 0xFFFF)) for x in u[i:i + 4]])
+        else:
+            out.append([(int(r >> 16), int(r & 0xFFFF))])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_packed_work_list_matches_definition(seed):
+    """The packed list holds the plain list's items in the same order: the items of more than
+    pack_tokens tokens one per row, then the rest four per row (the last row padded with
+    sequence 0xFFFF), every stored item referenced by exactly one row."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(100 + seed)
+    bs = int(rng.choice([8, 16, 64]))
+    part = int(rng.choice([p for p in (64, 128, 256, 512, 2048) if p % bs == 0]))
+    width = int(rng.integers(1, 300))
+    lens = rng.integers(-3, width * bs + 40, size=int(rng.integers(0, 200)))
+    pack = int(rng.integers(1, part // 4 + 1))
+    plain = expected(lens, width, bs, part)
+    lst, rows = pk.decode_work_list_packed(lens, width, bs, part, pack)
+    got = unpack(lst, rows)
+    ntok = {}
+    for b, L in enumerate(lens):
+        L = min(max(int(L), 0), width * bs)
+        for p in range(max(1, -(-L // part))):
+            ntok[(b, p)] = min(part, L - p * part)
+    nshort = sum(1 for it in plain if ntok[it] <= pack)
+    single = [r for r in got if len(r) == 1]
+    groups = [r for r in got if len(r) == 4]
+    assert len(single) + len(groups) == rows and got[:len(single)] == single
+    assert [r[0] for r in single] == plain[:len(plain) - nshort]
+    flat = [it for r in groups for it in r]
+    assert flat[:nshort] == plain[len(plain) - nshort:]
+    assert all(it == (0xFFFF, 0) for it in flat[nshort:]) and len(flat) - nshort < 4
+    assert len(lst) == rows + len(flat)
+    assert all(ntok[it] > pack for it in plain[:len(plain) - nshort])
+    # pack_tokens 0: the plain list, every entry a row
+    lst0, rows0 = pk.decode_work_list_packed(lens, width, bs, part, 0)
+    assert rows0 == len(lst0) and decode(lst0) == plain
+
+
+def test_packed_work_list_errors():
+    import ctypes
+    from paged_kv_cache_402_amd import _lib
+    lens = np.array([0, 512, 513, 1500], np.int32)
+    P = ctypes.POINTER(ctypes.c_int32)
+    lp = lens.ctypes.data_as(P)
+    rows = ctypes.c_int(-1)
+    f = _lib.lib.pkv_decode_work_list_packed
+    assert f(lp, 4, 200, 16, 512, 128, None, 0, ctypes.byref(rows)) == 10 and rows.value == 6
+    assert f(lp, 4, 200, 16, 512, 129, None, 0, ctypes.byref(rows)) == -1     # > part / 4
+    assert f(lp, 4, 200, 16, 512, -1, None, 0, ctypes.byref(rows)) == -1
+    assert f(lp, 4, 200, 16, 512, 64, None, 0, None) == -1                    # null rows
+    small = np.zeros(9, np.int32)
+    assert f(lp, 4, 200, 16, 512, 128, small.ctypes.data_as(P), 9, ctypes.byref(rows)) == -1
+    # sequences are limited to 32767 in every list (an item's top bit marks a packed row)
+    big = np.zeros(32768, np.int32)
+    assert f(big.ctypes.data_as(P), 32768, 4, 16, 64, 16, None, 0, ctypes.byref(rows)) == -1
+    assert _lib.lib.pkv_decode_work_list(big.ctypes.data_as(P), 32768, 4, 16, 64, None, 0) == -1
+    assert _lib.lib.pkv_decode_work_list(big.ctypes.data_as(P), 32767, 4, 16, 64, None, 0) == 32767
+
+
 def _shared_tables(rng, lens, width, bs, share_blocks, members):
     """Random private tables, then the first share_blocks entries of every member replaced by
     member 0's (the planner reads nothing but these arrays)."""

@@ -359,8 +359,21 @@ def llama3_8b_long_shared_prefix_case(num_seqs: int = 256, values: bool = True,
     return case
 
 
+def llama3_8b_short_batch_case(num_seqs: int = 2048, values: bool = True, poison: bool = True,
+                               max_len: int = 48) -> PagedDecodeCase:
+    """The GQA 8B shape (32 query / 8 KV heads, head_dim 128, block 16, bf16) on a large batch
+    of short sequences, lengths uniform on [1, 48]: the early decode steps of many requests
+    with short prompts, where every partition is short and the launch is bound by latency.
+    Private blocks from a pool of 1.25x the need."""
+    rng = np.random.default_rng(SEED_BASE + 6)
+    lens = rng.integers(1, max_len + 1, size=num_seqs).astype(np.int32)
+    return make_case("llama3_8b_short_batch_b%d_bf16" % num_seqs, rng, lens, 32, 8, 128, 16,
+                     "bf16", width=-(-max_len // 16), values=values, poison=poison)
+
+
 WORKLOADS = {
     "tiny": tiny_case,
+    "llama3_8b_short_batch": llama3_8b_short_batch_case,
     "llama3_8b_long_shared_prefix": llama3_8b_long_shared_prefix_case,
     "llama2_7b_mha": llama2_7b_mha_case,
     "llama3_8b_gqa_prefix": llama3_8b_gqa_prefix_case,
