@@ -554,7 +554,7 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), flush=True)
         sys.exit(2)
     if args.fork_tree or args.prefix_cache:

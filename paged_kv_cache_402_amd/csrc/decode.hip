@@ -11,12 +11,13 @@
 //
 // Work decomposition (our design for gfx950; the pages give no kernel structure):
 //   * one 256-lane workgroup (4 waves) per (KV head, context partition of `part` tokens,
-//     sequence). Grid x is the KV head: workgroups are dealt to the 8 XCDs round-robin, so
-//     with 8 KV heads every workgroup of one head runs on one XCD and blocks shared by many
-//     sequences (a common prompt prefix) stay in that XCD's L2. Grid y is the partition and
-//     z the sequence, so the partitions of one sequence are dispatched together and the
-//     partitions that cover a shared prefix are spread over the whole launch instead of all
-//     running first;
+//     sequence). Over a host work list (the usual launch) the grid is one-dimensional: row
+//     r of the list takes workgroups r * Hkv .. r * Hkv + Hkv - 1, one per KV head; the list
+//     holds only partitions that have tokens, full ones first, then the shorter last ones,
+//     longest first. Without a list the grid is (Hkv, partitions, sequences). Either way
+//     consecutive workgroups differ in KV head and workgroups are dealt to the 8 XCDs
+//     round-robin, so with 8 KV heads every workgroup of one head runs on one XCD and blocks
+//     shared by many sequences (a common prompt prefix) stay in that XCD's L2;
 //   * each wave owns a quarter of the partition and works through it on its own: no
 //     workgroup barrier until the final merge, so the four waves never wait for each other
 //     and their loads stay in flight independently. A packed row of the work list instead
@@ -27,16 +28,18 @@
 //   * K pass: LK lanes (8, or 16 for rows of more than 256 bytes) own one token row; each
 //     lane loads 16-byte vectors of it and takes the dot products with its slices of the G
 //     query rows of the GQA group (v_dot2 for 16-bit data, held in registers), finished by a
-//     DPP butterfly inside the lane group; UK steps of loads are issued before any use. The
-//     scores (in log2 units) go to the wave's own LDS area;
+//     DPP butterfly inside the lane group; UK steps of loads are issued before any use. At
+//     G = 8 with 16-bit data the scores come from the matrix cores instead (16 tokens x 16
+//     padded heads per v_mfma_f32_16x16x32). The scores (in log2 units) go to the wave's own
+//     LDS area;
 //   * the wave's max, then 2^(s - max) once per (token, head) and the exponent sum; the
 //     first round of V loads is issued before this step so it overlaps it;
 //   * V pass: LV lanes (16) own one token row; each lane accumulates p * v for its 8 (or 4)
 //     columns and every head of the group in fp32;
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
-//     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence that fits one partition gets its output row
-//     directly, longer ones leave (max, sum, accumulator) partials that a second kernel
-//     merges (deterministic split-K, no atomics).
+//     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence
+//     that fits one partition gets its output row directly, longer ones leave (max, sum,
+//     accumulator) partials that a second kernel merges (deterministic split-K, no atomics).
 // Tokens past the sequence end, and blocks whose table entry lies outside the pool, are
 // excluded by selects and branches, never by multiplying by zero (the slots may hold NaN).
 // The arithmetic order does not depend on where blocks sit in the pool.
@@ -596,8 +599,8 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) 
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
   (void)kv_dtype;
   // per wave: its scores (part / 4 x group floats), reused for its merge data afterwards
-  const size_t per = (size_t)(part / kDecodeWaves > head_dim + 2 ? part / kDecodeWaves : head_dim + 2);
-  return (size_t)kDecodeWaves * per * group * 4;
+  const int per = part / kDecodeWaves > head_dim + 2 ? part / kDecodeWaves : head_dim + 2;
+  return (size_t)kDecodeWaves * (size_t)per * (size_t)group * 4;
 }
 
 template <int DT, int D, int G>
