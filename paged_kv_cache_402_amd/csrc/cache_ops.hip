@@ -42,8 +42,11 @@ hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream)
   return hipGetLastError();
 }
 
-// One workgroup per (pair, 4096 vectors of the block); each lane moves 16 B per step.
+// One workgroup per (pair, 4096 vectors of the block); each lane moves 16 B of K and of V per
+// step and issues the loads of kCopyUnroll steps before their stores (src and dst are
+// different blocks, so the loads never read what the stores write).
 constexpr int kCopyVecsPerGroup = 4096;
+constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   const int pr = blockIdx.x;
@@ -58,11 +61,24 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   const unsigned char* vs = (const unsigned char*)a.v_cache + so;
   unsigned char* kd = (unsigned char*)a.k_cache + dof;
   unsigned char* vd = (unsigned char*)a.v_cache + dof;
-  for (int64_t i = v0 + threadIdx.x; i < v1; i += 256) {
-    const u32x4 x = load16(ks + i * 16);
-    const u32x4 y = load16(vs + i * 16);
-    store16(kd + i * 16, x);
-    store16(vd + i * 16, y);
+  for (int64_t i0 = v0 + threadIdx.x; i0 < v1; i0 += 256 * kCopyUnroll) {
+    u32x4 x[kCopyUnroll], y[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * 256;
+      if (i < v1) {
+        x[u] = load16(ks + i * 16);
+        y[u] = load16(vs + i * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * 256;
+      if (i < v1) {
+        store16(kd + i * 16, x[u]);
+        store16(vd + i * 16, y[u]);
+      }
+    }
   }
 }
 
