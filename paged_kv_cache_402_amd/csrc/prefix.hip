@@ -21,8 +21,16 @@
 // its new maximum needs no data movement.
 //
 // Softmax weights p are fp32; the value product takes them as two 16-bit operands, p = hi +
-// lo with hi = p rounded and lo = (p - hi) rounded, so the weights keep about 16 significant
-// bits (a single 16-bit p would err by up to 2^-9 relative per weight).
+// lo with hi = p truncated to 16 bits and lo = (p - hi) truncated, so the weights keep about
+// 15 significant bits with bf16 and 21 with fp16 (a single bf16 p would err by up to 2^-8
+// relative per weight).
+//
+// The pass is bound by VALU issue (two waves per SIMD), so the per-step arithmetic is kept
+// short: the weights use a reference max that moves only when a row's max passes it by more
+// than 8 (log2 units), so the accumulators, which live in the matrix-core registers, are
+// rescaled rarely instead of every step (weights then reach 2^8, which fp32 sums and the
+// 16-bit halves carry with the same relative precision); v_exp_f32 directly; the row max
+// over the four lanes of a row through lane swaps instead of LDS shuffles.
 
 #include <math.h>
 
@@ -47,17 +55,33 @@ template <> __device__ __forceinline__ f32x4 mma<F16>(u32x4 a, u32x4 b, f32x4 c)
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// p -> (hi, lo) 16-bit halves with p ~= hi + lo; returns the two 16-bit patterns packed.
-template <int DT> __device__ __forceinline__ void split16(float p, uint32_t& hi, uint32_t& lo);
-template <> __device__ __forceinline__ void split16<BF16>(float p, uint32_t& hi, uint32_t& lo) {
-  hi = narrow_bits<BF16>(p);
-  lo = narrow_bits<BF16>(p - as_f32(hi << 16));
+// (p0, p1) -> packed 16-bit halves hi = (hi0, hi1) and lo = (lo0, lo1) with p ~= hi + lo:
+// hi is p truncated, lo the exact fp32 remainder p - hi, truncated in turn.
+template <int DT> __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi,
+                                                            uint32_t& lo);
+template <>
+__device__ __forceinline__ void split_pair<BF16>(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h0 = as_u32(p0) & 0xFFFF0000u, h1 = as_u32(p1) & 0xFFFF0000u;
+  hi = __builtin_amdgcn_perm(h1, h0, 0x07060302u);        // upper halves of h0, h1
+  lo = __builtin_amdgcn_perm(as_u32(p1 - as_f32(h1)), as_u32(p0 - as_f32(h0)), 0x07060302u);
 }
-template <> __device__ __forceinline__ void split16<F16>(float p, uint32_t& hi, uint32_t& lo) {
-  const _Float16 h = (_Float16)p;
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, (_Float16)(p - (float)h));
+template <>
+__device__ __forceinline__ void split_pair<F16>(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(p0, p1);      // round toward zero
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - (float)h[0], p1 - (float)h[1]));
 }
+
+// max over lanes l, l ^ 16, l ^ 32 and l ^ 48: each swap leaves every lane with its own and its
+// partner's value in the two results
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = fmaxf(x, fmaxf(as_f32(a[0]), as_f32(a[1])));
+  const auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(x, fmaxf(as_f32(b[0]), as_f32(b[1])));
+}
+
+constexpr float kRescaleSlack = 8.f;      // log2 units a row's max may pass its reference
 
 constexpr int kD = 128;                   // head_dim of this pass
 constexpr int kRow = kD * 2;              // bytes of one token row of one head
@@ -133,8 +157,8 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
   const int vp = tid & 15;
   const int vc = tid >> 4;
   auto load_step = [&](int step, u32x4 (&x)[4]) {
-    const int tok = step * 32 + 2 * vp;
-    const size_t o0 = row_off(tok) + 16 * vc, o1 = row_off(tok + 1) + 16 * vc;
+    const int tok = step * 32 + 2 * vp;                   // even: tok + 1 is in the same block
+    const size_t o0 = row_off(tok) + 16 * vc, o1 = o0 + kRow;
     x[0] = load16(kbase + o0);
     x[1] = load16(kbase + o1);
     x[2] = load16(vbase + o0);
@@ -147,10 +171,10 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
     unsigned char* dst = s_vt[buf] + (size_t)(8 * vc) * kVtStride + 4 * vp;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // element e of token tok and of token tok + 1, packed: one byte permute
       const uint32_t w0 = x[2][e >> 1], w1 = x[3][e >> 1];
-      const uint32_t x0 = (e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-      const uint32_t x1 = (e & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(dst + e * kVtStride) = x0 | (x1 << 16);
+      *reinterpret_cast<uint32_t*>(dst + e * kVtStride) =
+          __builtin_amdgcn_perm(w1, w0, (e & 1) ? 0x07060302u : 0x05040100u);
     }
   };
 
@@ -193,31 +217,33 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
     float mx = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = xor_max_from<16>(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = row4_max(mx);
+    // move the reference max of the rows whose max passed it by more than the slack (all rows
+    // at the first step), rescaling what they have summed so far
+    const bool move = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    }
     uint32_t ph[4], pl[4];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(sc[e] - m_new), p1 = exp2f(sc[e + 1] - m_new);
+      // sc - m_run <= 8: the weights stay below 2^8; those under 2^-126 flush to zero
+      const float p0 = __builtin_amdgcn_exp2f(sc[e] - m_run);
+      const float p1 = __builtin_amdgcn_exp2f(sc[e + 1] - m_run);
       psum += p0 + p1;
-      uint32_t h0, l0, h1, l1;
-      split16<DT>(p0, h0, l0);
-      split16<DT>(p1, h1, l1);
-      ph[e >> 1] = h0 | (h1 << 16);
-      pl[e >> 1] = l0 | (l1 << 16);
+      split_pair<DT>(p0, p1, ph[e >> 1], pl[e >> 1]);
     }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
     const u32x4 bhi = u32x4{ph[0], ph[1], ph[2], ph[3]};
     const u32x4 blo = u32x4{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 c = acc[t] * alpha;
-      c = mma<DT>(av[t], bhi, c);
-      acc[t] = mma<DT>(av[t], blo, c);
-    }
+    for (int t = 0; t < NT; ++t) acc[t] = mma<DT>(av[t], blo, mma<DT>(av[t], bhi, acc[t]));
   };
 
   // Loads run kPf steps ahead of the math through a ring of registers; the LDS tiles are
