@@ -594,6 +594,36 @@ def test_shared_prefix_decode_matches_oracle(dtype, hq, hkv, bs, part, share, n)
     assert max_err(got, plain) <= 1e-4
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_shared_prefix_rescales_on_rising_scores(dtype):
+    """Scores that jump by far more than the pass's rescale slack in later steps of a shared
+    partition (and one far below everything else): the weights are taken against a reference
+    max that must move several times mid-partition. Every member's query heads of a group are
+    one vector u; shared keys at four tokens are u scaled by 1, 4, 8 and 12 (scores of about
+    15, 59, 119 and 178 in log2 units): kept against the first reference, the last weights
+    would pass 2^128 and overflow fp32, so the test fails unless the reference moves. One key
+    is -5 u."""
+    from oracle.storage import to_f64
+    hq, hkv, bs, part, share, n = 32, 8, 16, 512, 1024, 13
+    G = hq // hkv
+    rng = np.random.default_rng(52)
+    lens = [int(x) for x in rng.integers(share + 1, share + 900, size=n)] + [700]
+    case = _share_case("rise", 53, lens, hq, hkv, bs, dtype, share, list(range(n)))
+    u = rng.standard_normal((hkv, 128)).astype(np.float32)
+    q = np.repeat(u, G, axis=0)                               # [hq][128]: group heads equal
+    case.q = np.broadcast_to(gen.round_to_storage(q, dtype), case.q.shape).copy()
+    uq = to_f64(gen.round_to_storage(u, dtype), dtype)
+    for tok, f in ((40, 1.0), (300, 4.0), (600, 8.0), (900, 12.0), (1000, -5.0)):
+        blk = case.block_tables[0, tok // bs]
+        case.k_cache[blk, :, tok % bs, :] = gen.round_to_storage((f * uq).astype(np.float32), dtype)
+    got, plain, mem, pp = _run_shared(case, part)
+    assert mem.tolist() == list(range(n)) and pp == share // part
+    ref = oracle(case)
+    assert np.isfinite(got).all()
+    assert max_err(got, ref) <= GATE[dtype]
+    assert max_err(got, plain) <= 1e-4
+
+
 def test_shared_prefix_full_size_gqa_prefix_sampled():
     import paged_kv_cache_402_amd as pk
     case = gen.llama3_8b_gqa_prefix_case(values=False)
