@@ -622,7 +622,9 @@ def main():
     K, W = args.steps, args.warmup
     # the step's stages in launch order; one event before the first and one after each stage
     # that runs, so a stage's time is the span between its neighbouring events
-    fused = args.append == "fused" and members is None
+    # (with --grid shared the new token always lies in a sequence's own partitions, which the
+    # fused per-partition pass covers; the shared-prefix pass never reads it)
+    fused = args.append == "fused"
     if fused:
         # the new rows are stored by the decode pass: 2 * B * Hkv * d * eb more bytes written
         bytes_["decode_kernel"] += bytes_["cache_write"] // 2

@@ -624,6 +624,47 @@ def test_shared_prefix_rescales_on_rising_scores(dtype):
     assert max_err(got, plain) <= 1e-4
 
 
+def test_shared_prefix_with_fused_append():
+    """The shared-prefix pass, then the per-partition pass over the planner's list storing the
+    step's new tokens, then the merge: caches bitwise those of reshape_and_cache, the output
+    that of the plain decode over the written caches (each member's new token lies in its own
+    partitions, which the shared pass never reads)."""
+    import paged_kv_cache_402_amd as pk
+    dtype, hq, hkv, bs, part, share, n = "bf16", 32, 8, 16, 256, 512, 12
+    rng = np.random.default_rng(54)
+    lens = [int(x) for x in rng.integers(share + 1, share + 700, size=n)] + [share + 1, 90]
+    case = _share_case("shapp", 55, lens, hq, hkv, bs, dtype, share, list(range(n + 1)))
+    B, W = len(lens), case.block_tables.shape[1]
+    k_new, v_new = gen.normal(rng, (B, hkv, 128), dtype), gen.normal(rng, (B, hkv, 128), dtype)
+    slots = np.array([int(case.block_tables[b, (L - 1) // bs]) * bs + (L - 1) % bs
+                      for b, L in enumerate(lens)], np.int32)
+    mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, bs, part)
+    assert pp == share // part and mem.size == n + 1
+    q, tables, lns = to_dev(case.q, dtype), i32(case.block_tables), i32(case.seq_lens)
+    kn, vn = to_dev(k_new, dtype), to_dev(v_new, dtype)
+    k1, v1 = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    pk.reshape_and_cache(kn, vn, k1, v1, i32(slots))
+    plain = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode(plain, q, k1, v1, tables, lns, case.scale, partition_size=part)
+    k2, v2 = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    out = torch.full_like(plain, float("nan"))
+    ws = torch.empty(pk.decode_workspace_bytes(B, hq, W, bs, 128, part), dtype=torch.uint8,
+                     device="cuda")
+    pk.paged_attention_prefix(q, k2, v2, tables, lns, case.scale, i32(mem), pp, ws,
+                              partition_size=part)
+    pk.paged_attention_partitions_append(out, q, kn, vn, k2, v2, tables, lns, case.scale,
+                                         partition_size=part, workspace=ws, work_list=i32(items))
+    pk.paged_attention_reduce(out, lns, bs, W, ws, partition_size=part)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    assert float((out - plain).abs().max()) <= 1e-4
+    ref = gen.PagedDecodeCase("shapp", dtype, hq, hkv, 128, bs, case.num_blocks, case.seq_lens,
+                              case.block_tables, case.scale, q=case.q,
+                              k_cache=to_host(k2, dtype), v_cache=to_host(v2, dtype))
+    assert max_err(out.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
+
+
 def test_shared_prefix_full_size_gqa_prefix_sampled():
     import paged_kv_cache_402_amd as pk
     case = gen.llama3_8b_gqa_prefix_case(values=False)
