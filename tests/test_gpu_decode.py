@@ -119,6 +119,31 @@ def test_zero_length_and_single_token():
     _check(case)
 
 
+def test_largest_batches():
+    """The largest batches each launch form takes: 65535 sequences on the full grid (its
+    sequence dimension) and 32767 over a work list (an item's top bit is reserved), one or two
+    tokens each. A one-token sequence's output is its V row exactly (e^0 = 1); a two-token one
+    is checked against the oracle on a sample."""
+    import paged_kv_cache_402_amd as pk
+    for B, use_list in ((65535, False), (32767, True)):
+        rng = np.random.default_rng(B)
+        lens = (1 + (np.arange(B) % 2)).astype(np.int32)
+        case = gen.make_case("maxb", rng, lens, 2, 1, 64, 8, "f32", width=1, poison=False)
+        q, k, v = to_dev(case.q, "f32"), to_dev(case.k_cache, "f32"), to_dev(case.v_cache, "f32")
+        out = torch.full((B, 2, 64), float("nan"), dtype=torch.float32, device="cuda")
+        work = i32(pk.decode_work_list(lens, 1, 8, 32)) if use_list else None
+        pk.paged_attention_decode(out, q, k, v, i32(case.block_tables), i32(lens), case.scale,
+                                  partition_size=32, work_list=work)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        one = np.nonzero(lens == 1)[0]
+        rows = case.v_cache[case.block_tables[one, 0], 0, 0, :]          # [n][64]
+        assert np.array_equal(got[one, 0], rows) and np.array_equal(got[one, 1], rows)
+        seqs = [1, 3, B // 2 | 1, B - 2 if (B - 2) % 2 else B - 1]
+        ref = oracle(case, seqs=seqs)
+        assert max_err(got[seqs].astype(np.float64), ref[seqs]) <= GATE["f32"]
+
+
 def test_seq_lens_beyond_table_are_clamped():
     rng = np.random.default_rng(6)
     case = gen.make_case("clamp", rng, [48, 20], 4, 4, 64, 16, "f32", width=3)
