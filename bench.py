@@ -102,17 +102,17 @@ def build_forked_state(pk, gen, torch, dev):
         for br in range(1, fc.branches):
             bm.fork(parent, parent + br)
     B = fc.num_seqs
-    slots, pairs = bm.append_slots(range(B))
+    slots, pairs, cow_src = bm.append_step(range(B))
     tables, seq_lens = bm.build_tables(range(B), fc.table_width)
     case = gen.PagedDecodeCase(fc.name, fc.dtype, fc.num_q_heads, fc.num_kv_heads, fc.head_dim, bs,
                                nb, seq_lens, tables, fc.scale,
                                meta={"cow_pairs": int(pairs.shape[0]), "branches": fc.branches})
-    return case, bm, slots, pairs
+    return case, bm, slots, pairs, cow_src
 
 
 def build_state(name, pk, gen, torch, dev):
     if name == "llama13b_longtail":
-        case, bm, slots, pairs = build_forked_state(pk, gen, torch, dev)
+        case, bm, slots, pairs, cow_src = build_forked_state(pk, gen, torch, dev)
         B = case.num_seqs
         shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
         seed = 402100
@@ -129,6 +129,7 @@ def build_state(name, pk, gen, torch, dev):
             "slots": torch.from_numpy(slots).to(dev),
             "pairs": torch.from_numpy(np.ascontiguousarray(pairs.reshape(-1, 2))).to(dev)
             if pairs.shape[0] else None,
+            "cow_src": torch.from_numpy(cow_src).to(dev),
             "out": torch.empty((B, case.num_q_heads, case.head_dim), dtype=tdt, device=dev),
         }
     maker = gen.WORKLOADS[name]
@@ -625,10 +626,18 @@ def main():
     # (with --grid shared the new token always lies in a sequence's own partitions, which the
     # fused per-partition pass covers; the shared-prefix pass never reads it)
     fused = args.append == "fused"
+    # with the cache write fused, the copies of copy-on-write blocks are fused too
+    fused_cow = fused and st["pairs"] is not None
     if fused:
         # the new rows are stored by the decode pass: 2 * B * Hkv * d * eb more bytes written
         bytes_["decode_kernel"] += bytes_["cache_write"] // 2
-    stages = (["copy_blocks"] if st["pairs"] is not None else []) + \
+    if fused_cow:
+        # and the copies: every copied block's rows but the new token's, K and V, written
+        # (their reads are the attention's own, from the source block)
+        eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+        row = case.num_kv_heads * case.head_dim * eb
+        bytes_["decode_kernel"] += int(st["pairs"].shape[0]) * 2 * (case.block_size - 1) * row
+    stages = (["copy_blocks"] if st["pairs"] is not None and not fused_cow else []) + \
         ([] if fused else ["reshape_and_cache"]) + \
         (["shared_prefix"] if members is not None and pp > 0 else []) + \
         ["decode_partitions"] + (["partition_reduce"] if ws_bytes > 0 else [])
@@ -643,6 +652,11 @@ def main():
         elif name == "shared_prefix":
             pk.paged_attention_prefix(st["q"], st["k"], st["v"], st["tables"], st["lens"],
                                       case.scale, members, pp, ws, partition_size=part)
+        elif name == "decode_partitions" and fused_cow:
+            pk.paged_attention_partitions_step(st["out"], st["q"], st["k_new"], st["v_new"],
+                                               st["cow_src"], st["k"], st["v"], st["tables"],
+                                               st["lens"], case.scale, partition_size=part,
+                                               workspace=ws, work_list=work)
         elif name == "decode_partitions" and fused:
             pk.paged_attention_partitions_append(st["out"], st["q"], st["k_new"], st["v_new"],
                                                  st["k"], st["v"], st["tables"], st["lens"],

@@ -225,6 +225,38 @@ int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* 
                                           int work_items, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
+/* One decode step in one pass (P1 §6.2, §4.3; P2 §2.2): the copy-on-write of each sequence's
+ * last block, the cache write of its new token and the attention. cow_src (device int32
+ * [num_seqs]) names, for each sequence whose last block the block manager has just made a
+ * private copy of (pkv_bm_append_slot returned 1), the block it copied from (cow_src of that
+ * call; the table already lists the copy), and -1 for the others; entries outside the pool
+ * are ignored. For such a sequence the workgroup of each KV head that holds the new token
+ * copies that head's part of the source block into the sequence's last block (every row but
+ * the new token's, which it then stores from k_new / v_new), and reads the earlier tokens of
+ * that block from the source. Caches and output are bitwise those of pkv_copy_blocks, then
+ * pkv_reshape_and_cache, then the decode. Precondition (what a fork gives): in this launch the
+ * source block is written only at that same new-token row, by the sequence that kept it.
+ * Otherwise as pkv_paged_attention_decode_append. */
+int pkv_paged_attention_decode_step(void* out, int out_dtype, const void* q, const void* k_new,
+                                    const void* v_new, const int32_t* cow_src, void* k_cache,
+                                    void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                    const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, float scale,
+                                    int partition_size, const int32_t* work_list, int work_items,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+/* Its per-partition pass alone (the merge is pkv_paged_attention_reduce). */
+int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
+                                        const void* k_new, const void* v_new,
+                                        const int32_t* cow_src, void* k_cache, void* v_cache,
+                                        int kv_dtype, const int32_t* block_tables,
+                                        const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, int max_blocks_per_seq, float scale,
+                                        int partition_size, const int32_t* work_list,
+                                        int work_items, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Shared-prefix decode (P1 §6.1; P3 §2.2.3, §2.2.8: sequences that start with the same
  * prompt list the same physical blocks). The leading partitions that a group of sequences

@@ -53,6 +53,17 @@ SIGNATURES = {
                                                       c_int, c_int, c_int, c_int, c_float, c_int,
                                                       c_void_p, c_int, c_void_p, c_size_t,
                                                       c_void_p]),
+    "pkv_paged_attention_decode_step": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                                c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                                c_int, c_int, c_float, c_int, c_void_p, c_int,
+                                                c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attention_partitions_step": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
+                                                    c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_int, c_void_p, c_void_p, c_int, c_int,
+                                                    c_int, c_int, c_int, c_int, c_int, c_float,
+                                                    c_int, c_void_p, c_int, c_void_p, c_size_t,
+                                                    c_void_p]),
     "pkv_decode_plan_shared_prefix": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
                                               P_i32, P_int, P_int, P_i32, c_int]),
     "pkv_paged_attention_decode_shared": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,

@@ -116,6 +116,22 @@ class BlockManager:
               "append_slots")
         return slots, pairs[:ncow.value].copy()
 
+    def append_step(self, seqs):
+        """append_slots plus, per listed sequence, the block its last block was copied from
+        (-1 if none): the cow_src argument of paged_attention_decode_step. The manager
+        reports the copies in sequence order, each with the block the new slot lies in as
+        its destination. Returns (slots, cow_pairs, cow_src int32 [n])."""
+        slots, pairs = self.append_slots(seqs)
+        cow_src = np.full(slots.shape[0], -1, dtype=np.int32)
+        k = 0
+        for i, slot in enumerate(slots.tolist()):
+            if k < pairs.shape[0] and int(pairs[k, 1]) == slot // self.block_size:
+                cow_src[i] = pairs[k, 0]
+                k += 1
+        if k != pairs.shape[0]:
+            raise RuntimeError("append_step: copy pairs out of sequence order")
+        return slots, pairs, cow_src
+
     def table(self, seq: int):
         """(physical block ids, length in tokens)."""
         ntok = ctypes.c_int(0)

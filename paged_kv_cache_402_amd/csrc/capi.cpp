@@ -123,6 +123,7 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.work = nullptr;
   a.work_items = 0;
   a.k_new = nullptr;
+  a.cow_src = nullptr;
   a.v_new = nullptr;
   pl->group = group;
   pl->ws_needed = need;
@@ -493,6 +494,48 @@ int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* 
                        max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
   if (st != PKV_OK || num_seqs == 0) return st;
   if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  return partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
+}
+
+int pkv_paged_attention_decode_step(void* out, int out_dtype, const void* q, const void* k_new,
+                                    const void* v_new, const int32_t* cow_src, void* k_cache,
+                                    void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                    const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int max_blocks_per_seq, float scale,
+                                    int partition_size, const int32_t* work_list, int work_items,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  if (!cow_src) return fail(PKV_EINVAL, "decode_step: null cow_src");
+  pl.args.cow_src = cow_src;
+  st = partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
+                                        const void* k_new, const void* v_new,
+                                        const int32_t* cow_src, void* k_cache, void* v_cache,
+                                        int kv_dtype, const int32_t* block_tables,
+                                        const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, int max_blocks_per_seq, float scale,
+                                        int partition_size, const int32_t* work_list,
+                                        int work_items, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  if (!cow_src) return fail(PKV_EINVAL, "partitions_step: null cow_src");
+  pl.args.cow_src = cow_src;
   return partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
 }
 

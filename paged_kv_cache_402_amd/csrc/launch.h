@@ -38,6 +38,10 @@ struct DecodeArgs {
   // here instead of the cache and stored into the cache by the pass (null: none).
   const void* k_new;
   const void* v_new;
+  // Optional, with k_new: per sequence, the block its last block was just made a private copy
+  // of (-1: none). The pass copies it (this KV head's tile, all rows but the new token's)
+  // into the sequence's last block and reads the earlier tokens from it (null: no copies).
+  const int32_t* cow_src;
 };
 
 // Bytes of dynamic LDS one decode workgroup needs.

@@ -283,6 +283,57 @@ def paged_attention_partitions_append(out, q, k_new, v_new, k_cache, v_cache, bl
     return ws
 
 
+def _cow_arg(cow_src, B):
+    _i32(cow_src, "cow_src")
+    if tuple(cow_src.shape) != (B,):
+        raise ValueError("cow_src must be int32 [num_seqs]")
+    return cow_src.data_ptr()
+
+
+def paged_attention_decode_step(out, q, k_new, v_new, cow_src, k_cache, v_cache, block_tables,
+                                seq_lens, scale, partition_size=None, workspace=None,
+                                work_list=None):
+    """One decode step in one pass plus the merge: each sequence's copy-on-write of its last
+    block (cow_src int32 [B]: the source block, or -1), the cache write of its newest token
+    (k_new / v_new) and the attention; bitwise copy_blocks, then reshape_and_cache, then
+    paged_attention_decode. Returns `out`."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    partition_size = _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list)
+    _append_args(k_new, v_new, k_cache, B)
+    cs = _cow_arg(cow_src, B)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_decode_step(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_decode_step")
+    return out
+
+
+def paged_attention_partitions_step(out, q, k_new, v_new, cow_src, k_cache, v_cache,
+                                    block_tables, seq_lens, scale,
+                                    partition_size: int = DEFAULT_PARTITION, workspace=None,
+                                    work_list=None):
+    """First pass of paged_attention_decode_step only. Returns the workspace for
+    paged_attention_reduce."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    _append_args(k_new, v_new, k_cache, B)
+    cs = _cow_arg(cow_src, B)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_partitions_step(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
+        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        "paged_attention_partitions_step")
+    return ws
+
+
 def paged_attention_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, members,
                            prefix_partitions: int, workspace,
                            partition_size: int = DEFAULT_PARTITION):

@@ -75,6 +75,23 @@ def test_decode_rejects_bad_arguments_on_host(kw, code):
     assert _lib.last_error() != ""
 
 
+def test_decode_step_rejects_missing_or_misaligned_inputs_on_host():
+    """The fused step checks k_new / v_new and cow_src before any launch (fake device
+    addresses: nothing is dereferenced)."""
+    from paged_kv_cache_402_amd import _lib
+    f = _lib.lib.pkv_paged_attention_decode_step
+
+    def call(k_new=32, v_new=32, cow=64):
+        return f(16, 2, 16, k_new, v_new, cow, 16, 16, 2, 16, 16, 4, 32, 8, 128, 16, 100, 8, 0.1,
+                 512, None, 0, None, 0, None)
+    assert call(cow=None) == -1 and "cow_src" in _lib.last_error()
+    assert call(k_new=None) == -1
+    assert call(v_new=8) == -1                      # misaligned
+    g = _lib.lib.pkv_paged_attention_partitions_step
+    assert g(16, 2, 16, 32, 32, None, 16, 16, 2, 16, 16, 4, 32, 8, 128, 16, 100, 8, 0.1, 512,
+             None, 0, None, 0, None) == -1
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert _decode(B=0) == 0
 

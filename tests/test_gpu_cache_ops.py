@@ -364,3 +364,117 @@ def test_continuous_batching_loop_decodes_every_step():
     assert _bits_equal(kd, host_k, dt) and _bits_equal(vd, host_v, dt)
     assert worst <= GATE[dt]
     assert sched.stats()["finished"] == len(reqs) and preempted > 0
+
+
+# ------------------------------------------------------------------------------------------
+# one decode step in one pass: copy-on-write, cache write and attention fused
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,hq,hkv,bs,part,form", [
+    ("bf16", 32, 8, 16, 512, "list"),
+    ("f16", 40, 40, 32, 2048, "packed"),
+    ("bf16", 64, 8, 64, 1024, "full"),         # G 8: matrix-core scores
+    ("f32", 8, 4, 8, 64, "list"),
+])
+def test_decode_step_is_copy_then_cache_write_then_decode(dtype, hq, hkv, bs, part, form):
+    """Prompts forked into 1-4 branches, then one token each: branches of a partial last
+    block copy it (all but the last writer), full ones open a fresh block. The fused step
+    (decode_step with the manager's per-sequence copy sources) must leave bitwise the caches
+    and the output of copy_blocks, reshape_and_cache and the decode run apart. Unwritten slots
+    hold NaN, so a read of a copy before it is made would show."""
+    P = pk()
+    rng = np.random.default_rng(80)
+    d = 128 if dtype != "f32" else 64
+    prompts = [3 * bs - 3, 2 * bs, part + 5, 1, 0, bs + 1, 2 * part - 1, 7]
+    branches = [4, 3, 2, 1, 2, 4, 3, 1]
+    nb = 8 + sum(-(-(L + 1) // bs) * br + 1 for L, br in zip(prompts, branches))
+    bm = P.BlockManager(nb, bs, rng.permutation(nb).astype(np.int32))
+    kd = to_dev(np.full((nb, hkv, bs, d), gen.nan_value(dtype),
+                        dtype=gen.storage_numpy_dtype(dtype)), dtype)
+    vd = kd.clone()
+    seqs = []
+    for g, (L, br) in enumerate(zip(prompts, branches)):
+        parent = 10 * g
+        bm.add_seq(parent, L)
+        if L:
+            P.reshape_and_cache(to_dev(gen.normal(rng, (L, hkv, d), dtype), dtype),
+                                to_dev(gen.normal(rng, (L, hkv, d), dtype), dtype), kd, vd,
+                                i32(bm.slots(parent, 0, L)))
+        seqs.append(parent)
+        for b in range(1, br):
+            bm.fork(parent, parent + b)
+            seqs.append(parent + b)
+    B = len(seqs)
+    slots, pairs, cow_src = bm.append_step(seqs)
+    assert pairs.shape[0] == sum(br - 1 for L, br in zip(prompts, branches) if L % bs)
+    W = max(-(-(L + 1) // bs) for L in prompts) + 1
+    tables, lens = bm.build_tables(seqs, W)
+    q = to_dev(gen.normal(rng, (B, hq, d), dtype), dtype)
+    k_new = to_dev(gen.normal(rng, (B, hkv, d), dtype), dtype)
+    v_new = to_dev(gen.normal(rng, (B, hkv, d), dtype), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    if form == "full":
+        work = None
+    elif form == "list":
+        work = i32(P.decode_work_list(lens, W, bs, part))
+    else:
+        lst, rows = P.decode_work_list_packed(lens, W, bs, part, part // 4)
+        assert rows < len(lst)
+        work = (i32(lst), rows)
+    # apart
+    k1, v1 = kd.clone(), vd.clone()
+    if pairs.shape[0]:
+        P.copy_blocks(k1, v1, i32(pairs.reshape(-1, 2)))
+    P.reshape_and_cache(k_new, v_new, k1, v1, i32(slots))
+    o1 = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    P.paged_attention_decode(o1, q, k1, v1, i32(tables), i32(lens), scale, partition_size=part,
+                             work_list=work)
+    # fused
+    k2, v2 = kd.clone(), vd.clone()
+    o2 = torch.full_like(o1, float("nan"))
+    P.paged_attention_decode_step(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
+                                  i32(lens), scale, partition_size=part, work_list=work)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    assert torch.equal(o1, o2)
+    ref = gen.PagedDecodeCase("step", dtype, hq, hkv, d, bs, nb, lens, tables, scale,
+                              q=to_host(q, dtype), k_cache=to_host(k2, dtype),
+                              v_cache=to_host(v2, dtype))
+    assert max_err(o2.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
+
+
+def test_decode_step_long_tail_parallel_sampling():
+    """The long-tail serving step at full size (32 prompts x 4 branches, 40 MHA heads, fp16,
+    block 32): the fused step over the work list against the separate copy, cache write and
+    decode, bitwise."""
+    P = pk()
+    c = gen.llama13b_longtail_case(values=False)
+    nb, bs, H, d, B = c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim, c.num_seqs
+    bm = P.BlockManager(nb, bs, c.free_order)
+    for g, L in enumerate(c.decode_lens.tolist()):
+        bm.add_seq(g * c.branches, L - 1)
+        for br in range(1, c.branches):
+            bm.fork(g * c.branches, g * c.branches + br)
+    slots, pairs, cow_src = bm.append_step(range(B))
+    assert (cow_src >= 0).sum() == pairs.shape[0] > 0
+    tables, lens = bm.build_tables(range(B), c.table_width)
+    shape = (nb, H, bs, d)
+    kd, vd = gen.device_normal(shape, "f16", 81, "cuda"), gen.device_normal(shape, "f16", 82, "cuda")
+    q = gen.device_normal((B, H, d), "f16", 83, "cuda")
+    k_new, v_new = gen.device_normal((B, H, d), "f16", 84, "cuda"), gen.device_normal((B, H, d), "f16", 85, "cuda")
+    work = i32(P.decode_work_list(lens, c.table_width, bs, 2048))
+    k1, v1 = kd.clone(), vd.clone()
+    P.copy_blocks(k1, v1, i32(pairs.reshape(-1, 2)))
+    P.reshape_and_cache(k_new, v_new, k1, v1, i32(slots))
+    o1 = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
+    P.paged_attention_decode(o1, q, k1, v1, i32(tables), i32(lens), c.scale, partition_size=2048,
+                             work_list=work)
+    k2, v2 = kd.clone(), vd.clone()
+    o2 = torch.empty_like(o1)
+    P.paged_attention_decode_step(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
+                                  i32(lens), c.scale, partition_size=2048, work_list=work)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
