@@ -218,42 +218,48 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const unsigned char* knew = fused ? (const unsigned char*)a.k_new + new_off : nullptr;
   const unsigned char* vnew = fused ? (const unsigned char*)a.v_new + new_off : nullptr;
   // copy-on-write of the last block (optional): the block the sequence shared until this
-  // step's append; this KV head's tile of it is copied into the new private block, all rows
-  // but the new token's (which the store below writes), and the earlier tokens are then read
-  // from it (the copy is bitwise theirs). The four waves copy together (a packed wave copies
-  // its own item's tile), eight 16-byte loads in flight per lane before their stores.
+  // step's append. The earlier tokens of the last block are read from it (the copy would be
+  // bitwise theirs), and after the output is written this KV head's tile of it is copied into
+  // the new private block, all rows but the new token's (which the store below writes): the
+  // source's rows are then in L2 from the attention's own reads. The four waves copy
+  // together (a packed wave copies its own item's tile), eight 16-byte loads in flight per
+  // lane before their stores.
   const int cow = (fused && a.cow_src != nullptr && last >= 0 && last < n) ? a.cow_src[b] : -1;
-  if ((unsigned)cow < (unsigned)a.num_blocks) {
-    const int blk = pick_id(ids, last >> a.bs_log2);
-    if ((unsigned)blk < (unsigned)a.num_blocks) {
-      const size_t so = (size_t)cow * block_bytes + kvh * head_bytes;
-      const size_t dof = (size_t)blk * block_bytes + kvh * head_bytes;
-      const int nvec = K::C << a.bs_log2;                  // 16-byte vectors of one tile
-      const int skip = last & bs_mask;
-      const int first = packed ? lane : tid;
-      const int stride = packed ? 64 : NT;
-      constexpr int kBatch = 8;
-      for (int c0 = first; c0 < 2 * nvec; c0 += kBatch * stride) {
-        u32x4 x[kBatch];
+  const int cow_dst =
+      (unsigned)cow < (unsigned)a.num_blocks ? pick_id(ids, last >> a.bs_log2) : -1;
+  auto cow_copy = [&]() {
+    if ((unsigned)cow < (unsigned)a.num_blocks) {
+      const int blk = cow_dst;
+      if ((unsigned)blk < (unsigned)a.num_blocks) {
+        const size_t so = (size_t)cow * block_bytes + kvh * head_bytes;
+        const size_t dof = (size_t)blk * block_bytes + kvh * head_bytes;
+        const int nvec = K::C << a.bs_log2;                  // 16-byte vectors of one tile
+        const int skip = last & bs_mask;
+        const int first = packed ? lane : tid;
+        const int stride = packed ? 64 : NT;
+        constexpr int kBatch = 8;
+        for (int c0 = first; c0 < 2 * nvec; c0 += kBatch * stride) {
+          u32x4 x[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int c = c0 + u * stride;
-          const int cc = c >= nvec ? c - nvec : c;
-          if (c < 2 * nvec && cc / K::C != skip)
-            x[u] = load16((const unsigned char*)(c >= nvec ? a.v_cache : a.k_cache) + so +
-                          (size_t)cc * 16);
-        }
+          for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u * stride;
+            const int cc = c >= nvec ? c - nvec : c;
+            if (c < 2 * nvec && cc / K::C != skip)
+              x[u] = load16((const unsigned char*)(c >= nvec ? a.v_cache : a.k_cache) + so +
+                            (size_t)cc * 16);
+          }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int c = c0 + u * stride;
-          const int cc = c >= nvec ? c - nvec : c;
-          if (c < 2 * nvec && cc / K::C != skip)
-            store16((unsigned char*)(c >= nvec ? a.v_cache : a.k_cache) + dof + (size_t)cc * 16,
-                    x[u]);
+          for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u * stride;
+            const int cc = c >= nvec ? c - nvec : c;
+            if (c < 2 * nvec && cc / K::C != skip)
+              store16((unsigned char*)(c >= nvec ? a.v_cache : a.k_cache) + dof + (size_t)cc * 16,
+                      x[u]);
+          }
         }
       }
     }
-  }
+  };
   if (fused && last >= 0 && last < n && (packed || wave == 0)) {
     const int blk = pick_id(ids, last >> a.bs_log2);
     if ((unsigned)blk < (unsigned)a.num_blocks) {
@@ -514,6 +520,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         }
       }
     }
+    cow_copy();
     return;
   }
   // every lane's score reads are done before the area is reused (LDS keeps a wave's order)
@@ -564,6 +571,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       }
     }
   }
+  cow_copy();
 }
 
 // Merge of the partitions of one (sequence, query head):
