@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk",
-                   "llama13b_longtail", "llama3_8b_long_shared_prefix", "llama3_8b_short_batch")
+                   "llama13b_longtail", "llama3_8b_long_shared_prefix", "llama3_8b_short_batch",
+                   "tiny")
 
 
 def parse_args():
