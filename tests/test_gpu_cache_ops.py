@@ -256,12 +256,14 @@ def test_prefix_cached_requests_decode_over_shared_blocks():
         assert max_err(got[s], ref) <= GATE["bf16"]
 
 
-@pytest.mark.parametrize("width,part", [(4, 512), (3, 32)])
-def test_beam_search_loop_decodes_every_step(width, part):
+@pytest.mark.parametrize("width,part,fused", [(4, 512, False), (3, 32, False), (4, 512, True),
+                                              (3, 32, True)])
+def test_beam_search_loop_decodes_every_step(width, part, fused):
     """P2 §2.2 / P1 §6.2: beam search over 40 steps on a tight pool (finished beams' blocks are
     handed out again): every step frees the dropped beams, forks the kept ones, appends one
     token per beam (copy-on-write of shared partial blocks), writes the new K/V and decodes all
-    beams. Device caches stay bit-identical to the oracle's, and every decode matches it."""
+    beams, as three launches or (fused) as one decode step. Device caches stay bit-identical
+    to the oracle's, and every decode matches it."""
     from workloads import traces
     P = pk()
     rng = np.random.default_rng(402700 + width)
@@ -288,16 +290,18 @@ def test_beam_search_loop_decodes_every_step(width, part):
             bm.fork(p_, c_)
             model.fork(p_, c_)
         seqs = step.appends
-        sl, pairs = bm.append_slots(seqs)
+        sl, pairs, cow_src = bm.append_step(seqs)
         res = [model.append_slot(s) for s in seqs]
         assert sl.tolist() == [r[1] for r in res]
         ref_pairs = [[r[2], r[3]] for r in res if r[0] == 1]
         assert pairs.reshape(-1, 2).tolist() == ref_pairs
         if ref_pairs:
-            P.copy_blocks(kd, vd, i32(pairs.reshape(-1, 2)))
+            if not fused:
+                P.copy_blocks(kd, vd, i32(pairs.reshape(-1, 2)))
             host_k, host_v = ref_ops.copy_blocks(host_k, host_v, ref_pairs)
         nk, nv = gen.normal(rng, (len(seqs), H, d), dt), gen.normal(rng, (len(seqs), H, d), dt)
-        P.reshape_and_cache(to_dev(nk, dt), to_dev(nv, dt), kd, vd, i32(sl))
+        if not fused:
+            P.reshape_and_cache(to_dev(nk, dt), to_dev(nv, dt), kd, vd, i32(sl))
         host_k, host_v = ref_ops.reshape_and_cache(nk, nv, host_k, host_v, sl.tolist())
         tables, lens = bm.build_tables(seqs, W)
         for i, s in enumerate(seqs):
@@ -306,7 +310,16 @@ def test_beam_search_loop_decodes_every_step(width, part):
         q = gen.normal(rng, (len(seqs), Hq, d), dt)
         case = gen.PagedDecodeCase("beam", dt, Hq, H, d, bs, NB, lens, tables, 0.0884, q=q,
                                    k_cache=host_k, v_cache=host_v)
-        got, _ = run_decode(case, k=kd, v=vd, partition_size=part)
+        if fused:
+            out = torch.full((len(seqs), Hq, d), float("nan"), dtype=torch.float32,
+                             device="cuda")
+            P.paged_attention_decode_step(out, to_dev(q, dt), to_dev(nk, dt), to_dev(nv, dt),
+                                          i32(cow_src), kd, vd, i32(tables), i32(lens), 0.0884,
+                                          partition_size=part)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+        else:
+            got, _ = run_decode(case, k=kd, v=vd, partition_size=part)
         worst = max(worst, max_err(got, oracle(case)))
         torch.cuda.synchronize()
         assert _bits_equal(kd, host_k, dt) and _bits_equal(vd, host_v, dt)
