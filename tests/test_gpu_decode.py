@@ -144,6 +144,66 @@ def test_largest_batches():
         assert max_err(got[seqs].astype(np.float64), ref[seqs]) <= GATE["f32"]
 
 
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations_match_oracle(seed):
+    """Seeded draws over the supported space at once: dtype, head_dim, group, KV heads, block
+    size, partition size, batch and lengths (with 0, 1 and block/partition edges), launch form
+    (full grid, work list, packed list) and whether the step's new token is stored by the
+    pass. Each draw is checked against the oracle; with the store fused, the caches must also
+    be bitwise those of reshape_and_cache."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(9000 + seed)
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    d = int(rng.choice([64, 128, 256]))
+    G = int(rng.choice([1, 2, 4] if d == 256 else [1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    bs = int(rng.choice([8, 16, 32, 64]))
+    parts = [p for p in (32, 64, 128, 256, 512, 1024, 2048) if p % bs == 0 and p >= bs]
+    part = int(rng.choice(parts))
+    B = int(rng.integers(1, 13))
+    edges = [1, bs - 1, bs, bs + 1, part, part + 1, 2 * part + 3]
+    lens = [int(rng.choice(edges)) if rng.random() < 0.5 else int(rng.integers(1, 3 * part))
+            for _ in range(B)]
+    form = ["full", "list", "packed"][(seed // 3) % 3]
+    fused = bool(seed % 2)
+    W = max(-(-L // bs) for L in lens) + 1
+    case = gen.make_case("rnd", rng, lens, G * hkv, hkv, d, bs, dtype, width=W)
+    q, k, v = to_dev(case.q, dtype), to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    tables, lns = i32(case.block_tables), i32(case.seq_lens)
+    if form == "full":
+        work = None
+    elif form == "list":
+        work = i32(pk.decode_work_list(case.seq_lens, W, bs, part))
+    else:
+        lst, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, part, part // 4)
+        work = (i32(lst), rows)
+    out = torch.full((B, G * hkv, d), float("nan"), dtype=torch.float32, device="cuda")
+    if fused:
+        # the last token's K/V come in as new rows; its slot is poisoned beforehand
+        nk = case.k_cache[case.block_tables[np.arange(B), (np.array(lens) - 1) // bs], :,
+                          (np.array(lens) - 1) % bs, :].copy()
+        nv = case.v_cache[case.block_tables[np.arange(B), (np.array(lens) - 1) // bs], :,
+                          (np.array(lens) - 1) % bs, :].copy()
+        want_k, want_v = k.clone(), v.clone()
+        for b, L in enumerate(lens):
+            blk = int(case.block_tables[b, (L - 1) // bs])
+            k[blk, :, (L - 1) % bs, :] = float("nan")
+            v[blk, :, (L - 1) % bs, :] = float("nan")
+        pk.paged_attention_decode_append(out, q, to_dev(nk, dtype), to_dev(nv, dtype), k, v,
+                                         tables, lns, case.scale, partition_size=part,
+                                         work_list=work)
+    else:
+        pk.paged_attention_decode(out, q, k, v, tables, lns, case.scale, partition_size=part,
+                                  work_list=work)
+    torch.cuda.synchronize()
+    if fused:
+        assert torch.equal(k.view(torch.uint8), want_k.view(torch.uint8))
+        assert torch.equal(v.view(torch.uint8), want_v.view(torch.uint8))
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert max_err(got, oracle(case)) <= GATE[dtype], (dtype, d, G, hkv, bs, part, form, fused)
+
+
 def test_seq_lens_beyond_table_are_clamped():
     rng = np.random.default_rng(6)
     case = gen.make_case("clamp", rng, [48, 20], 4, 4, 64, 16, "f32", width=3)
