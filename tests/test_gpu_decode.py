@@ -750,6 +750,28 @@ def test_shared_prefix_with_fused_append():
     assert max_err(out.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_shared_prefix_random_configurations(seed):
+    """Seeded draws of the shared-prefix pass: dtype, group, block and partition size, shared
+    length (one to three partitions), group size, private lengths, plus sequences outside
+    the group; against the oracle and the per-partition path."""
+    rng = np.random.default_rng(9500 + seed)
+    dtype = ["bf16", "f16"][seed % 2]
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 8]))
+    bs = int(rng.choice([8, 16, 32, 64]))
+    part = int(rng.choice([p for p in (64, 128, 256, 512, 1024) if p % bs == 0 and p // bs <= 256]))
+    share = part * int(rng.integers(1, 4))
+    n = int(rng.integers(2, 40))
+    lens = [share + int(rng.integers(1, 700)) for _ in range(n)] + [int(rng.integers(1, 900))]
+    case = _share_case("srnd", 9600 + seed, lens, G * hkv, hkv, bs, dtype, share, list(range(n)))
+    got, plain, mem, pp = _run_shared(case, part)
+    assert mem.tolist() == list(range(n)) and pp == share // part
+    assert np.isfinite(got).all()
+    assert max_err(got, oracle(case)) <= GATE[dtype], (dtype, G, hkv, bs, part, share, n)
+    assert max_err(got, plain) <= 1e-4
+
+
 def test_shared_prefix_full_size_gqa_prefix_sampled():
     import paged_kv_cache_402_amd as pk
     case = gen.llama3_8b_gqa_prefix_case(values=False)
