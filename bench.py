@@ -740,6 +740,8 @@ def main():
                    "kv_dtype": case.dtype, "partition_size": part, "grid": args.grid,
                    "pack_tokens": args.pack if args.grid == "list" else 0,
                    "append": "fused" if fused else "separate",
+                   "copy_on_write": ("fused" if fused_cow else "separate")
+                   if st["pairs"] is not None else "none",
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),
                    "num_blocks": case.num_blocks, "parallelism": "single GPU"},
