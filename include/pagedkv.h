@@ -81,9 +81,10 @@ const char* pkv_last_error(void);
  * ========================================================================================== */
 
 /* Bytes of split-K workspace pkv_paged_attention_decode needs: for every (sequence, query
- * head, context partition) one running max, one exponent sum and one head_dim-long fp32
- * accumulator. partition_size defaults to 512 when 0 is passed. Returns 0 on bad input or
- * when no sequence can span two partitions. */
+ * head, context partition) one running max and one exponent sum (fp32 pairs, their area
+ * padded to a multiple of 16 bytes), then one head_dim-long fp32 accumulator. partition_size
+ * defaults to 512 when 0 is passed. Returns 0 on bad input or when no sequence can span two
+ * partitions. */
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
                                   int block_size, int head_dim, int partition_size);
 
@@ -99,7 +100,8 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_
  *   partition_size: tokens per context partition (split-K); a multiple of 32 and of
  *                  block_size in [32, 2048]; 0 selects 512. Sequences longer than one
  *                  partition are finished by a second, deterministic merge pass.
- *   workspace    : device buffer of at least pkv_decode_workspace_bytes() bytes; may be NULL
+ *   workspace    : 16-byte aligned device buffer of at least pkv_decode_workspace_bytes()
+ *                  bytes (else PKV_EWORKSPACE, or PKV_EINVAL if misaligned); may be NULL
  *                  only if workspace_bytes is 0 and no sequence can span two partitions
  *                  (max_blocks_per_seq*block_size <= partition_size). Calls that share a
  *                  workspace must not overlap in time (enqueue them on one stream).

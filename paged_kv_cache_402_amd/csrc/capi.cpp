@@ -53,6 +53,19 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Split-K workspace: (max, sum) floats [B][Hq][pmax][2], padded to a multiple of 16 bytes so
+// that the accumulators [B][Hq][pmax][D] floats after them take 16-byte loads. Nothing when no
+// sequence can span two partitions.
+struct WsLayout {
+  size_t acc_off, total;
+};
+WsLayout ws_layout(int64_t num_seqs, int64_t num_q_heads, int64_t pmax, int64_t head_dim) {
+  if (pmax <= 1) return {0, 0};
+  const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)pmax;
+  const size_t ml = (rows * 8 + 15) / 16 * 16;
+  return {ml, ml + rows * (size_t)head_dim * 4};
+}
+
 struct DecodePlan {
   DecodeArgs args;
   int group;
@@ -95,11 +108,12 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
     return fail(PKV_EINVAL, "decode: null pointer");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_EINVAL, "decode: q and caches must be 16-byte aligned");
-  size_t need = 0;
-  if (pmax > 1)
-    need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+  const WsLayout ws = ws_layout(num_seqs, num_q_heads, pmax, head_dim);
+  const size_t need = ws.total;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PKV_EINVAL, "decode: workspace must be 16-byte aligned");
 
   DecodeArgs& a = pl->args;
   a.out = out;
@@ -109,7 +123,7 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.ws_ml = reinterpret_cast<float*>(workspace);
-  a.ws_acc = need ? a.ws_ml + (size_t)num_seqs * num_q_heads * (size_t)pmax * 2 : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_off) : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -148,8 +162,7 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_
       head_dim <= 0 || partition_size <= 0)
     return 0;
   const int64_t pmax = ((int64_t)max_blocks_per_seq * block_size + partition_size - 1) / partition_size;
-  if (pmax <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
+  return ws_layout(num_seqs, num_q_heads, pmax, head_dim).total;
 }
 
 int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, const void* k_cache,
@@ -638,15 +651,16 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
   const int64_t pmax = ((int64_t)max_blocks_per_seq * block_size + partition_size - 1) / partition_size;
   if (pmax <= 1 || num_seqs == 0) return ok();  // nothing spans two partitions
   if (pmax > 65535) return fail(PKV_EINVAL, "reduce: too many partitions per sequence");
-  const size_t need = (size_t)num_seqs * num_q_heads * (size_t)pmax * (size_t)(head_dim + 2) * 4;
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_EWORKSPACE, "reduce: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  const WsLayout ws = ws_layout(num_seqs, num_q_heads, pmax, head_dim);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(PKV_EWORKSPACE, "reduce: workspace of %zu bytes needed, %zu given", ws.total, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PKV_EINVAL, "reduce: workspace must be 16-byte aligned");
   if (!out || !seq_lens) return fail(PKV_EINVAL, "reduce: null pointer");
   DecodeArgs a = {};
   a.out = out;
   a.seq_lens = seq_lens;
   a.ws_ml = (float*)workspace;
-  a.ws_acc = a.ws_ml + (size_t)num_seqs * num_q_heads * (size_t)pmax * 2;
+  a.ws_acc = (float*)((const char*)workspace + ws.acc_off);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.max_blocks = max_blocks_per_seq;

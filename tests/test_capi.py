@@ -67,6 +67,7 @@ def _decode(**kw):
     (dict(q=None), -1),
     (dict(W=64), -6),                       # 1024 tokens > one partition: workspace needed
     (dict(W=64, ws=16, wsb=10), -6),
+    (dict(W=64, ws=8, wsb=1 << 20), -1),    # workspace not 16-byte aligned
     (dict(D=256, Hq=64), -1),               # head_dim 256 with group 8
 ])
 def test_decode_rejects_bad_arguments_on_host(kw, code):
@@ -101,6 +102,9 @@ def test_workspace_size_formula():
     # 4 seqs x 32 heads x ceil(64*16/512)=2 partitions x (128 + 2) floats
     assert ops.decode_workspace_bytes(4, 32, 64, 16, 128, 512) == 4 * 32 * 2 * 130 * 4
     assert ops.decode_workspace_bytes(4, 32, 32, 16, 128, 512) == 0
+    # an odd number of (sequence, head, partition) rows: the (max, sum) pairs take 3 x 8 bytes,
+    # padded to 32 so the accumulators start 16-byte aligned
+    assert ops.decode_workspace_bytes(1, 1, 48, 16, 64, 256) == 32 + 3 * 64 * 4
 
 
 @pytest.mark.parametrize("call", ["rc_dtype", "rc_bs", "cb_dtype", "cb_null", "rc_align"])
