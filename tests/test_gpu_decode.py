@@ -376,7 +376,7 @@ def test_full_size_sampled(which):
 
 
 # --------------------------------------------------------------------------------------------
-# split-K: the one-launch merge (completion counters) and the two-launch form
+# split-K: a reused caller workspace and the two-launch form (partitions, then the merge)
 # --------------------------------------------------------------------------------------------
 
 def test_caller_workspace_reused_bitwise():
