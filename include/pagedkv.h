@@ -135,11 +135,13 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
                                int max_blocks_per_seq, int partition_size,
                                const void* workspace, size_t workspace_bytes, void* stream);
 
-/* A partition size for these shapes: the longest of 2048, 1024, 512 and 256 tokens whose
- * workgroup takes at most 40 KiB of LDS (four per compute unit) and that still gives at least
- * 1024 workgroups if every sequence were as long as its table allows (256 otherwise). Longer partitions mean fewer
- * workgroups, less fixed cost per token and fewer partials to merge; the floor keeps small
- * batches spread over the machine. Negative on bad arguments. */
+/* A partition size for these shapes: the longest multiple of 256 tokens up to 2048 (and a
+ * multiple of block_size) whose workgroup takes at most its share of a compute unit's LDS at
+ * the occupancy the kernel's registers allow (40 KiB, four per compute unit, up to 4 query
+ * heads per KV head; 53 KiB, three, at 8) and that still gives at least 1024 workgroups if
+ * every sequence were as long as its table allows (256 otherwise). Longer partitions mean
+ * fewer workgroups, less fixed cost per token and fewer partials to merge; the floor keeps
+ * small batches spread over the machine. Negative on bad arguments. */
 int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_blocks_per_seq);
 

@@ -273,17 +273,23 @@ int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads
     return fail(PKV_EINVAL, "default_partition: bad argument");
   const int group = num_q_heads / num_kv_heads;
   const int64_t tokens = (int64_t)max_blocks_per_seq * block_size;
-  // the longest partition whose workgroup leaves room for four per compute unit in the LDS
-  // (160 KiB each) and that still gives the machine work: at least kMinGroups workgroups
-  // even if every sequence were as long as its table allows
+  // the longest partition (a multiple of 256 tokens, and of the block size) whose workgroup
+  // takes no more than its share of a compute unit's 160 KiB of LDS at the occupancy the
+  // kernel's registers allow, and that still gives the machine work: at least kMinGroups
+  // workgroups even if every sequence were as long as its table allows. Up to G = 4 the
+  // kernels fit four workgroups per compute unit (40 KiB each); the G = 8 kernels hold more
+  // than 128 VGPRs, so three (53 KiB each): longer partitions there cost no occupancy.
   constexpr int64_t kMinGroups = 1024;
-  constexpr size_t kDefaultLds = 40 * 1024;
-  int part = 2048;
-  while (part > 256) {
-    const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((tokens + part - 1) / part);
-    if (decode_lds_bytes(PKV_BF16, head_dim, group, part) <= kDefaultLds && groups >= kMinGroups)
+  const size_t lds_share = group == 8 ? 160 * 1024 / 3 : 40 * 1024;
+  static const int kCandidates[] = {2048, 1792, 1536, 1280, 1024, 768, 512, 256};
+  int part = 256;
+  for (int c : kCandidates) {
+    if (c % block_size != 0) continue;
+    const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((tokens + c - 1) / c);
+    if (decode_lds_bytes(PKV_BF16, head_dim, group, c) <= lds_share && groups >= kMinGroups) {
+      part = c;
       break;
-    part /= 2;
+    }
   }
   ok();
   return part;

@@ -49,8 +49,8 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: 
 
 def default_partition(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                       block_size: int, max_blocks_per_seq: int) -> int:
-    """The partition size pkv_decode_default_partition picks for these shapes (2048, 1024, 512
-    or 256 tokens)."""
+    """The partition size pkv_decode_default_partition picks for these shapes (a multiple of
+    256 tokens up to 2048)."""
     return check(lib.pkv_decode_default_partition(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                   block_size, max_blocks_per_seq),
                  "default_partition")
