@@ -101,10 +101,19 @@ def test_block_sizes(bs):
     _check(case, partition_size=part)
 
 
-@pytest.mark.parametrize("part", [32, 64, 256, 512, 1024, 2048])
+@pytest.mark.parametrize("part", [32, 64, 256, 512, 768, 1024, 1536, 2048])
 def test_partition_sizes_agree(part):
     rng = np.random.default_rng(77)
     case = gen.make_case("part", rng, [1, 100, 700, 3000, 4500], 16, 4, 128, 16, "bf16")
+    _check(case, partition_size=part)
+
+
+@pytest.mark.parametrize("part", [1024, 1280, 1536])
+def test_partition_sizes_agree_group8(part):
+    """G = 8 on 64-token blocks (the long-context shape) at the partition sizes the default
+    policy can pick there, with ragged last partitions and a sequence of one token."""
+    rng = np.random.default_rng(78)
+    case = gen.make_case("part8", rng, [1, 64, 1535, 1537, 4000, 9000], 64, 8, 128, 64, "bf16")
     _check(case, partition_size=part)
 
 
@@ -158,7 +167,7 @@ def test_random_configurations_match_oracle(seed):
     G = int(rng.choice([1, 2, 4] if d == 256 else [1, 2, 4, 8]))
     hkv = int(rng.choice([1, 2, 4]))
     bs = int(rng.choice([8, 16, 32, 64]))
-    parts = [p for p in (32, 64, 128, 256, 512, 1024, 2048) if p % bs == 0 and p >= bs]
+    parts = [p for p in (32, 64, 128, 256, 512, 768, 1024, 1536, 2048) if p % bs == 0 and p >= bs]
     part = int(rng.choice(parts))
     B = int(rng.integers(1, 13))
     edges = [1, bs - 1, bs, bs + 1, part, part + 1, 2 * part + 3]
