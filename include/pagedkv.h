@@ -370,6 +370,15 @@ int pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src,
 int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
                         int32_t* cow_pairs, int* num_cow);
 
+/* pkv_bm_append_slots that also fills cow_src (int32[n], may be NULL): for each listed
+ * sequence, the block its last block was copied from by this append (the src of its
+ * copy-on-write pair), or -1 when its token went into a private or fresh block. That array is
+ * the cow_src argument of pkv_paged_attention_decode_step for the same batch order (P1 §6.2:
+ * a write into a shared block copies exactly that block first). On failure nothing changes,
+ * cow_src included. */
+int pkv_bm_append_step(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                       int32_t* cow_pairs, int* num_cow, int32_t* cow_src);
+
 /* Appends num_tokens tokens to the sequence, as that many pkv_bm_append_slot calls in a row
  * (prefill of a new chunk), atomically: on failure nothing changes. At most the first token
  * can need a copy-on-write; *cow_src / *cow_dst (may be NULL) receive it, or -1. The slots
@@ -455,7 +464,8 @@ typedef struct {
   int num_batch, num_slots, num_cow, num_finished, num_admitted, num_preempted;
 } pkv_sched_step_out;
 
-/* block_size must be the manager's; max_step_tokens >= max_num_seqs. NULL on bad input. */
+/* block_size must be the manager's (else NULL); max_step_tokens >= max_num_seqs. NULL on bad
+ * input. */
 pkv_sched* pkv_sched_create(pkv_bm* bm, int block_size, int max_num_seqs, int max_step_tokens,
                             int watermark_blocks);
 void pkv_sched_destroy(pkv_sched* s);
@@ -494,7 +504,8 @@ enum { PKV_UTIL_OF_REMAINDER = 0, PKV_UTIL_OF_DEVICE = 1 };
  * at once if each reserved max_model_len tokens contiguously = floor(pool / (out[1] *
  * max_model_len)). PKV_EINVAL for out-of-range arguments or num_blocks * block_size >=
  * 2^31 (slot ids are int32); PKV_ENOBLOCKS if the pool holds no block (out[0], [1], [2], [4]
- * are still filled). */
+ * are still filled; out[0] is negative when the weights and the reserve exceed the budget, and
+ * INT64_MIN when that shortfall is beyond the int64 range). */
 int pkv_kv_pool_plan(int64_t device_bytes, int64_t weight_bytes, int64_t reserve_bytes,
                      int32_t utilization_ppm, int utilization_of, int num_layers,
                      int num_kv_heads, int head_dim, int elem_bytes, int block_size,

@@ -86,6 +86,7 @@ SIGNATURES = {
     "pkv_bm_share_prefix": (c_int, [c_void_p, c_int64, c_int64, c_int]),
     "pkv_bm_append_slot": (c_int, [c_void_p, c_int64, P_i32, P_i32, P_i32]),
     "pkv_bm_append_slots": (c_int, [c_void_p, P_i64, c_int, P_i32, P_i32, P_int]),
+    "pkv_bm_append_step": (c_int, [c_void_p, P_i64, c_int, P_i32, P_i32, P_int, P_i32]),
     "pkv_bm_extend": (c_int, [c_void_p, c_int64, c_int, P_i32, P_i32]),
     "pkv_bm_free_seq": (c_int, [c_void_p, c_int64]),
     "pkv_bm_table": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),

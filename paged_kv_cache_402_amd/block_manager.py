@@ -118,19 +118,18 @@ class BlockManager:
 
     def append_step(self, seqs):
         """append_slots plus, per listed sequence, the block its last block was copied from
-        (-1 if none): the cow_src argument of paged_attention_decode_step. The manager
-        reports the copies in sequence order, each with the block the new slot lies in as
-        its destination. Returns (slots, cow_pairs, cow_src int32 [n])."""
-        slots, pairs = self.append_slots(seqs)
-        cow_src = np.full(slots.shape[0], -1, dtype=np.int32)
-        k = 0
-        for i, slot in enumerate(slots.tolist()):
-            if k < pairs.shape[0] and int(pairs[k, 1]) == slot // self.block_size:
-                cow_src[i] = pairs[k, 0]
-                k += 1
-        if k != pairs.shape[0]:
-            raise RuntimeError("append_step: copy pairs out of sequence order")
-        return slots, pairs, cow_src
+        (-1 if none): the cow_src argument of paged_attention_decode_step. Returns (slots,
+        cow_pairs, cow_src int32 [n])."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        cow_src = np.empty(max(n, 1), dtype=np.int32)
+        ncow = ctypes.c_int(0)
+        check(lib.pkv_bm_append_step(self._h, _p(s, ctypes.c_int64), n, _p(slots, ctypes.c_int32),
+                                     _p(pairs, ctypes.c_int32), ctypes.byref(ncow),
+                                     _p(cow_src, ctypes.c_int32)), "append_step")
+        return slots[:n], pairs[:ncow.value].copy(), cow_src[:n]
 
     def table(self, seq: int):
         """(physical block ids, length in tokens)."""

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpagedkv.so")
 
 SOURCES = ["decode.hip", "prefix.hip", "cache_ops.hip", "capi.cpp", "block_manager.cpp",
-           "scheduler.cpp", "pool_plan.cpp"]
+           "scheduler.cpp", "pool_plan.cpp", "errors.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

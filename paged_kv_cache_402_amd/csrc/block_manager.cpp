@@ -22,6 +22,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "bm_internal.h"
 #include "errors.h"
 #include "pagedkv.h"
 
@@ -129,6 +130,10 @@ std::string block_key_of(const pkv_bm* bm, int32_t parent, const int32_t* tokens
 }
 
 }  // namespace
+
+namespace pkv {
+int bm_block_size(const pkv_bm* bm) { return bm->block_size; }
+}  // namespace pkv
 
 namespace {
 
@@ -285,10 +290,10 @@ int pkv_bm_append_slot(pkv_bm* bm, int64_t seq, int32_t* slot, int32_t* cow_src,
   return st;
 }
 
-int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
-                        int32_t* cow_pairs, int* num_cow) {
+int pkv_bm_append_step(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                       int32_t* cow_pairs, int* num_cow, int32_t* cow_src) {
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_cow)
-    return pkv::fail(PKV_EINVAL, "append_slots: bad argument");
+    return pkv::fail(PKV_EINVAL, "append_step: bad argument");
   std::vector<AppendUndo> log(n);
   int ncow = 0;
   for (int i = 0; i < n; ++i) {
@@ -303,8 +308,16 @@ int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
       ++ncow;
     }
   }
+  // written only once the whole batch has succeeded, so a failure leaves it untouched
+  if (cow_src)
+    for (int i = 0; i < n; ++i) cow_src[i] = log[i].kind == 2 ? log[i].src : -1;
   *num_cow = ncow;
   return pkv::ok();
+}
+
+int pkv_bm_append_slots(pkv_bm* bm, const int64_t* seqs, int n, int32_t* slots,
+                        int32_t* cow_pairs, int* num_cow) {
+  return pkv_bm_append_step(bm, seqs, n, slots, cow_pairs, num_cow, nullptr);
 }
 
 int pkv_bm_extend(pkv_bm* bm, int64_t seq, int num_tokens, int32_t* cow_src, int32_t* cow_dst) {
@@ -343,7 +356,8 @@ int pkv_bm_table(const pkv_bm* bm, int64_t seq, int32_t* out, int cap, int* num_
   if (it == bm->seqs.end()) return pkv::fail(PKV_ENOSEQ, "table: unknown sequence %lld", (long long)seq);
   const auto& s = it->second;
   int n = (int)s.blocks.size();
-  std::memcpy(out, s.blocks.data(), sizeof(int32_t) * (size_t)(n < cap ? n : cap));
+  const int m = n < cap ? n : cap;
+  if (m > 0) std::memcpy(out, s.blocks.data(), sizeof(int32_t) * (size_t)m);
   if (num_tokens) *num_tokens = (int)s.tokens;
   pkv::ok();
   return n;
@@ -373,7 +387,7 @@ int pkv_bm_build_tables(const pkv_bm* bm, const int64_t* seqs, int n, int32_t* t
     const auto& s = it->second;
     if ((int)s.blocks.size() > width) return pkv::fail(PKV_EINVAL, "build_tables: table wider than %d", width);
     int32_t* row = tables + (size_t)i * width;
-    std::memcpy(row, s.blocks.data(), sizeof(int32_t) * s.blocks.size());
+    if (!s.blocks.empty()) std::memcpy(row, s.blocks.data(), sizeof(int32_t) * s.blocks.size());
     for (int j = (int)s.blocks.size(); j < width; ++j) row[j] = -1;
     seq_lens[i] = (int32_t)s.tokens;
   }

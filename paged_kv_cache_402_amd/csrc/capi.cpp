@@ -15,23 +15,6 @@
 
 namespace pkv {
 
-static thread_local std::string g_last_error;
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return code;
-}
-
-int ok() {
-  g_last_error.clear();
-  return PKV_OK;
-}
-
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
@@ -152,8 +135,6 @@ using namespace pkv;
 extern "C" {
 
 int pkv_version(void) { return 100; }
-
-const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
                                   int block_size, int head_dim, int partition_size) {

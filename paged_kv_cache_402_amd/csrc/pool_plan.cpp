@@ -56,13 +56,17 @@ extern "C" int pkv_kv_pool_plan(int64_t device_bytes, int64_t weight_bytes,
   // Bytes left for the pool. Either the fraction applies to what the weights and the reserve
   // leave over (the page's worked figure), or it caps everything the process may use and the
   // weights and the reserve come out of that cap.
-  int64_t pool = 0;
+  // (128-bit: weights and reserve near the int64 limit must not overflow; a shortfall beyond
+  // the int64 range is reported as INT64_MIN, and such a pool holds no block either way)
+  __int128 pool128 = 0;
   if (utilization_of == PKV_UTIL_OF_REMAINDER) {
-    const int64_t left = device_bytes - weight_bytes - reserve_bytes;
-    pool = left > 0 ? scale_ppm(left, utilization_ppm) : left;
+    const __int128 left = static_cast<__int128>(device_bytes) - weight_bytes - reserve_bytes;
+    pool128 = left > 0 ? scale_ppm(static_cast<int64_t>(left), utilization_ppm) : left;
   } else {
-    pool = scale_ppm(device_bytes, utilization_ppm) - weight_bytes - reserve_bytes;
+    pool128 = static_cast<__int128>(scale_ppm(device_bytes, utilization_ppm)) - weight_bytes -
+              reserve_bytes;
   }
+  const int64_t pool = pool128 < INT64_MIN ? INT64_MIN : static_cast<int64_t>(pool128);
   // at most 4096^3 * 2 * 4 = 2^39 bytes per token, 2^51 per block: no overflow in int64
   const int64_t per_token = static_cast<int64_t>(num_layers) * 2 * num_kv_heads * head_dim *
                             elem_bytes;

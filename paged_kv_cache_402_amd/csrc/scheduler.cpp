@@ -23,6 +23,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "bm_internal.h"
 #include "errors.h"
 #include "pagedkv.h"
 
@@ -60,6 +61,11 @@ pkv_sched* pkv_sched_create(pkv_bm* bm, int block_size, int max_num_seqs, int ma
   if (!bm || block_size <= 0 || max_num_seqs <= 0 || max_step_tokens < max_num_seqs ||
       watermark_blocks < 0) {
     pkv::fail(PKV_EINVAL, "sched_create: bad argument (max_step_tokens must be >= max_num_seqs)");
+    return nullptr;
+  }
+  if (block_size != pkv::bm_block_size(bm)) {
+    pkv::fail(PKV_EINVAL, "sched_create: block_size %d is not the manager's %d", block_size,
+              pkv::bm_block_size(bm));
     return nullptr;
   }
   auto* s = new pkv_sched();

@@ -88,6 +88,34 @@ def test_batch_append_is_atomic():
     assert slots.tolist() == [4 * 4 + 2] and pairs.tolist() == [[1, 4]]
 
 
+def test_append_step_names_each_sequence_copy_source():
+    """P1 §6.2 / P2 §2.2: branches forked from one prompt share its partial last block; the
+    first writers each copy it, the last holder writes in place. append_step reports the
+    source per listed sequence, in the listed order (not the order pairs were made)."""
+    bm = _bm(32, 4)
+    bm.add_seq(0, 6)                    # blocks 0, 1; block 1 half full
+    for c in (1, 2, 3):
+        bm.fork(0, c)
+    bm.add_seq(9, 8)                    # blocks 2, 3, both full: next token opens block 4
+    slots, pairs, cow_src = bm.append_step([3, 9, 1, 0, 2])
+    model = BlockManagerModel(32, 4)
+    model.add_seq(0, 6)
+    for c in (1, 2, 3):
+        model.fork(0, c)
+    model.add_seq(9, 8)
+    exp = [model.append_slot(s) for s in (3, 9, 1, 0, 2)]
+    assert slots.tolist() == [x[1] for x in exp]
+    assert cow_src.tolist() == [1, -1, 1, 1, -1]     # seq 2 is the last holder of block 1
+    assert pairs[:, 0].tolist() == [1, 1, 1]
+    # every copy's destination is the block the new slot lies in
+    dst = {s: slots[i] // 4 for i, s in enumerate((3, 9, 1, 0, 2))}
+    assert sorted(pairs[:, 1].tolist()) == sorted(dst[s] for s in (3, 1, 0))
+    assert bm.refcount(1) == 1 and bm.table(2)[0] == [0, 1]
+    # an empty batch returns empty arrays
+    s0, p0, c0 = bm.append_step([])
+    assert s0.shape == (0,) and p0.shape == (0, 2) and c0.shape == (0,)
+
+
 def test_build_tables_pads_with_minus_one():
     bm = _bm(8, 4)
     bm.add_seq(10, 5)
@@ -185,11 +213,17 @@ def test_matches_reference_model(nb, bs, seed, ops):
                     model.restore(snap)
                     model.alloc_failures = failures - sum(1 for x in res if x[0] < 0) + 1
                     with pytest.raises(Exception):
-                        cpp.append_slots(batch)
-                else:
+                        cpp.append_slots(batch) if r % 2 else cpp.append_step(batch)
+                elif r % 2:
                     slots, pairs = cpp.append_slots(batch)
                     assert slots.tolist() == [x[1] for x in res]
                     assert pairs.tolist() == [[x[2], x[3]] for x in res if x[0] == 1]
+                else:
+                    # the decode step's form: per entry, the block its append copied from
+                    slots, pairs, cow_src = cpp.append_step(batch)
+                    assert slots.tolist() == [x[1] for x in res]
+                    assert pairs.tolist() == [[x[2], x[3]] for x in res if x[0] == 1]
+                    assert cow_src.tolist() == [x[2] if x[0] == 1 else -1 for x in res]
         _same_state(cpp, model)
 
 
