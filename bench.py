@@ -64,6 +64,12 @@ def parse_args():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain block copy of known size (HBM counter calibration)")
+    p.add_argument("--read-probe", action="store_true",
+                   help="only measure plain HBM reads (pkv_read_probe): a 2 GiB stream, random "
+                        "tiles of 4-64 KiB from a 2.5 GiB pool, and the GQA 8B workload's "
+                        "pattern with a block's 8 heads read by 8 workgroups or by one")
+    p.add_argument("--no-read-probe", action="store_true",
+                   help="leave the short read probe (achievable_GBps) out of the headline run")
     p.add_argument("--warm", action="store_true",
                    help="time back-to-back steps by wall clock, leaving the previous step's "
                         "KV in L2 and the 256 MB memory-side cache (default: read a 1 GiB "
@@ -251,6 +257,19 @@ def byte_model(case, part):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ---------------------------------------------------------------------------------------------
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (platform.processor() is often just the
+    architecture)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(st, target_s, gen):
     from oracle import paged_attention as opa
     try:
@@ -295,8 +314,8 @@ def cpu_baseline(st, target_s, gen):
                       "the %d sequences in order until %.1f s; GB/s over each pass's distinct KV "
                       "bytes (a pass over the batch is one step), summed; host %s, %d "
                       "logical CPUs" % (done, case.num_q_heads, case.num_seqs, spent,
-                                        platform.processor() or platform.machine(),
-                                        len(os.sched_getaffinity(0))),
+                                        cpu_model(), len(os.sched_getaffinity(0))),
+            "cpu_model": cpu_model(), "logical_cpus": len(os.sched_getaffinity(0)),
             "seconds": round(spent, 3), "tokens_per_s": round(done / spent, 3)}
 
 
@@ -353,6 +372,80 @@ def copy_probe(pk, torch, dev):
     per = 2 * 4096 * H * bs * D * 2
     print(json.dumps({"copy_probe": True, "bytes_read_per_launch": per,
                       "bytes_written_per_launch": per, "launches": 5}), flush=True)
+
+
+PROBE_POOL_BYTES = 5 << 29          # 2.5 GiB: the GQA 8B pool's size, beyond the 256 MB MALL
+PROBE_READ_BYTES = 1820 << 20       # about the GQA 8B decode kernel's bytes per launch
+
+
+def probe_patterns(full):
+    """(name, tile_bytes, tile ids, tiles per workgroup, what it stands for). Seeded."""
+    rng = np.random.default_rng(402700)
+    pats = [("stream_2GiB", 64 << 10, np.arange((2 << 30) >> 16), 16,
+             "one 2 GiB contiguous read, 1 MiB per workgroup")]
+
+    def rand_tiles(tb, tpw):
+        n = PROBE_READ_BYTES // tb
+        ids = rng.choice(PROBE_POOL_BYTES // tb, n, replace=False)
+        return ("random_%dKiB" % (tb >> 10), tb, ids, tpw,
+                "%d distinct random %d KiB tiles of a 2.5 GiB pool, 1 MiB per workgroup"
+                % (n, tb >> 10))
+    pats.append(rand_tiles(4 << 10, 256))
+    if not full:
+        return pats
+    for tb in (8 << 10, 16 << 10, 64 << 10):
+        pats.append(rand_tiles(tb, (1 << 20) // tb))
+    # the GQA 8B workload's pattern: blocks of 8 KV heads x 4 KiB (32 KiB, one cache), a
+    # workgroup per (256-block item, KV head) with the heads of one item consecutive (so the
+    # 8 XCDs take one head each), against one workgroup reading 32 whole blocks
+    nblk = PROBE_READ_BYTES // (32 << 10) // 256 * 256
+    blocks = rng.choice(PROBE_POOL_BYTES // (32 << 10), nblk, replace=False)
+    items = blocks.reshape(-1, 256)
+    split = (items[:, None, :] * 8 + np.arange(8)[None, :, None]).reshape(-1)
+    pats.append(("gqa_heads_split_4KiB", 4 << 10, split, 256,
+                 "%d random 32 KiB blocks; workgroup (item of 256 blocks, head h) reads head "
+                 "h's 4 KiB of each; consecutive workgroups differ in head" % nblk))
+    pats.append(("gqa_heads_grouped_32KiB", 32 << 10, blocks, 32,
+                 "the same %d blocks; one workgroup reads 32 whole blocks" % nblk))
+    pats.append(("random_4KiB_one_per_group", 4 << 10,
+                 rng.choice(PROBE_POOL_BYTES >> 12, PROBE_READ_BYTES >> 12, replace=False), 1,
+                 "the same bytes as random_4KiB, one tile (4 KiB) per workgroup"))
+    return pats
+
+
+def read_probe(pk, torch, dev, full, reps=10):
+    """Plain-read bandwidth of each pattern: 2 warm-up launches, then `reps` launches, each
+    after a 1 GiB read of other data (cold L2 and memory-side cache, as the decode timing);
+    HIP events on the launch stream around each; GB/s = bytes read / median launch time."""
+    buf = torch.ones(PROBE_POOL_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    evict_sum = torch.zeros((), dtype=torch.float32, device=dev)
+    res = []
+    for name, tb, ids, tpw, what in probe_patterns(full):
+        d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
+        for _ in range(2):
+            pk.read_probe(buf, tb, d_ids, tpw, sink)
+        ts = []
+        for _ in range(reps):
+            torch.sum(evict, dim=0, out=evict_sum)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pk.read_probe(buf, tb, d_ids, tpw, sink)
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ts])
+        nbytes = int(len(ids)) * tb
+        res.append({"pattern": name, "bytes": nbytes, "tile_bytes": tb,
+                    "workgroups": -(-len(ids) // tpw), "median_ms": round(float(np.median(ms)), 5),
+                    "GBps": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
+                    "GBps_p10_p90": [round(nbytes / (float(np.percentile(ms, q)) * 1e-3) / 1e9, 1)
+                                     for q in (90, 10)],
+                    "what": what})
+        log("read probe %s: %.1f GB/s" % (name, res[-1]["GBps"]))
+    del buf, evict
+    return res
 
 
 def serve_loop(pk, torch, dev, steps, static=False, warm_steps=None):
@@ -573,6 +666,10 @@ def main():
     if args.copy_probe:
         copy_probe(pk, torch, dev)
         return
+    if args.read_probe:
+        print(json.dumps({"read_probe": read_probe(pk, torch, dev, full=True),
+                          "peak_GBps": HBM_PEAK_GBPS}), flush=True)
+        return
     if args.serve:
         serve_report(pk, torch, dev, args.serve_steps)
         return
@@ -651,7 +748,7 @@ def main():
         elif name == "reshape_and_cache":
             pk.reshape_and_cache(st["k_new"], st["v_new"], st["k"], st["v"], st["slots"])
         elif name == "shared_prefix":
-            pk.paged_attention_prefix(st["q"], st["k"], st["v"], st["tables"], st["lens"],
+            pk.paged_attention_prefix(st["out"], st["q"], st["k"], st["v"], st["tables"], st["lens"],
                                       case.scale, members, pp, ws, partition_size=part)
         elif name == "decode_partitions" and fused_cow:
             pk.paged_attention_partitions_step(st["out"], st["q"], st["k_new"], st["v_new"],
@@ -700,7 +797,8 @@ def main():
     t1 = time.perf_counter()
     ms_wall = (t1 - t0) * 1e3 / K
     # cold: the step's own span between its first and last event (the eviction sits before it)
-    ms_step = ms_wall if args.warm else float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
+    step_ms = np.array([e[0].elapsed_time(e[-1]) for e in ev])
+    ms_step = ms_wall if args.warm else float(np.mean(step_ms))
     per = {name: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, name in enumerate(stages)}
     stage_ms = {name: round(float(np.mean(per[name])), 5) if name in per else None
                 for name in ("decode_partitions", "partition_reduce", "copy_blocks",
@@ -725,6 +823,9 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 5),
+                                round(float(np.percentile(step_ms, 90)), 5)],
         "timing": "wall clock over back-to-back steps (warm caches)" if args.warm else
                   ("HIP events around each step, 1 GiB read before each (cold L2 and "
                    "memory-side cache); wall clock incl. the eviction reads %.4f ms/step"
@@ -732,19 +833,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": case.dtype,
         "data": "synthetic (seeded N(0,1) K/V/Q on the device; seeded lengths and placement)",
         "config": {"workload": case.name, "num_seqs": case.num_seqs,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
-                   "kv_dtype": case.dtype, "partition_size": part, "grid": args.grid,
+                   "kv_dtype": case.dtype, "accumulate": "f32", "partition_size": part,
+                   "grid": args.grid,
                    "pack_tokens": args.pack if args.grid == "list" else 0,
                    "append": "fused" if fused else "separate",
                    "copy_on_write": ("fused" if fused_cow else "separate")
                    if st["pairs"] is not None else "none",
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),
-                   "num_blocks": case.num_blocks, "parallelism": "single GPU"},
+                   "num_blocks": case.num_blocks, "parallelism": "single GPU",
+                   **({"named_partition_size": 512,
+                       "partition_note": "the workload's definition names 512-token partitions; "
+                                         "run with --partition 512 for that form (the default "
+                                         "partition of the library's policy is faster)"}
+                      if case.name == "long_context_splitk" and part != 512 else {})},
         "decode_tokens_per_s": round(case.num_seqs / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "kv_unique_bytes": bytes_["kv_unique"],
@@ -755,8 +862,20 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(case.name),
                      "kernel": "paged_decode_partition_kernel",
+                     "scope": "the decode partition kernel alone, per launch; the whole "
+                              "step's fraction is frac_of_hbm_peak",
                      "bytes_per_launch": kernel_bytes},
     }
+    if not args.no_read_probe:
+        log("read probe (achievable read bandwidth)")
+        probe = read_probe(pk, torch, dev, full=False)
+        ach = probe[0]["GBps"]
+        result["achievable_GBps"] = ach
+        result["achievable_note"] = ("plain 2 GiB streaming read measured on this device "
+                                     "(pkv_read_probe), beside the nominal %.0f GB/s peak"
+                                     % HBM_PEAK_GBPS)
+        result["frac_of_achievable"] = round(gbps / ach, 4)
+        result["read_probe"] = probe
     log("host manager cost")
     result["host_manager_us_per_step"] = round(host_manager_cost(pk, case), 1)
     if not args.no_cpu_baseline:

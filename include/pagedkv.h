@@ -291,11 +291,15 @@ int pkv_decode_plan_shared_prefix(const int32_t* block_tables, const int32_t* se
  * prefix_partitions come from pkv_decode_plan_shared_prefix, or from a caller that knows
  * the sharing (the block manager's forks and shared prefixes): every member must list the
  * first member's block ids in its first prefix_partitions * partition_size / block_size
- * table entries and be longer than prefix_partitions * partition_size tokens, and work_list
- * must hold every other partition exactly once. The shared-prefix pass needs fp16 or bf16
- * KV, head_dim 128 and partition_size / block_size <= 256 (else PKV_EINVAL); the workspace
- * is the one pkv_decode_workspace_bytes sizes. Members naming a sequence outside the batch
- * are skipped. */
+ * table entries, and work_list must hold every other partition of every sequence (those of
+ * non-members, and the members' partitions past the shared ones) exactly once. Each member
+ * attends only to its own seq_lens[b] tokens, so a member may end inside the shared
+ * partitions (the planner never picks one); one that fits a single partition gets its output
+ * row from the shared-prefix pass itself. Table entries outside the pool are left out with
+ * their tokens, as in the per-partition pass. The shared-prefix pass needs fp16 or bf16 KV,
+ * head_dim 128 and partition_size / block_size <= 256 (else PKV_EINVAL); the workspace is
+ * the one pkv_decode_workspace_bytes sizes. Members naming a sequence outside the batch are
+ * skipped. */
 int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
                                       const void* k_cache, const void* v_cache, int kv_dtype,
                                       const int32_t* block_tables, const int32_t* seq_lens,
@@ -307,14 +311,15 @@ int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
                                       int work_items, void* workspace, size_t workspace_bytes,
                                       void* stream);
 /* The shared-prefix pass alone (for timing or scheduling apart): writes the members'
- * partials of the shared partitions into the workspace. */
-int pkv_paged_attention_prefix(const void* q, const void* k_cache, const void* v_cache,
-                               int kv_dtype, const int32_t* block_tables, const int32_t* seq_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int num_blocks, int max_blocks_per_seq,
-                               float scale, int partition_size, const int32_t* members,
-                               int num_members, int prefix_partitions, void* workspace,
-                               size_t workspace_bytes, void* stream);
+ * partials of the shared partitions into the workspace, and the output row (out, of
+ * out_dtype: kv_dtype or PKV_F32) of any member that fits one partition. */
+int pkv_paged_attention_prefix(void* out, int out_dtype, const void* q, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                               const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, float scale, int partition_size,
+                               const int32_t* members, int num_members, int prefix_partitions,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Cache write (P1 §4.3; P3 §2.2.2-§2.2.3): token t's K and V rows ([num_kv_heads][head_dim],
  * contiguous, t-major) are copied bit for bit to slot slot_mapping[t] of k_cache / v_cache.
@@ -330,6 +335,19 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
 int pkv_copy_blocks(void* k_cache, void* v_cache, int dtype, const int32_t* src_dst_pairs,
                     int num_pairs, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, void* stream);
+
+/* Read-bandwidth probe (measurement only; no page defines it). The pages give no kernel
+ * figure, and decode is judged against HBM bandwidth: this call measures the read rate the
+ * device actually reaches, in the decode kernel's access patterns, as the achievable ceiling
+ * reported beside the nominal peak. One 256-lane workgroup per tiles_per_group (1..1024)
+ * consecutive entries of tile_ids (device int32 [num_tiles]); entry i names the tile_bytes
+ * (a power of two in [256, 1 MiB]) contiguous bytes at tile_ids[i] * tile_bytes of buf (device,
+ * 16-byte aligned, buf_bytes long); ids outside the buffer are skipped. Every byte of every
+ * listed tile is loaded once. sink (device uint32) is written only if a lane's fold of its
+ * loaded words equals sentinel. Enqueued on stream; no synchronisation. */
+int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
+                   int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
+                   void* stream);
 
 /* ==========================================================================================
  * Host block manager (P2 §3.1 manager sketch; P1 §4.1-§4.3, §6; P3 §2.2.2-§2.2.3)

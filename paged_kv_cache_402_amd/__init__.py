@@ -18,6 +18,7 @@ from .ops import (copy_blocks, decode_work_list, decode_work_list_packed,  # noq
                   paged_attention_decode_step, paged_attention_partitions_step,
                   paged_attention_partitions, paged_attention_partitions_append,
                   paged_attention_prefix,
-                  paged_attention_reduce, plan_shared_prefix, reshape_and_cache)
+                  paged_attention_reduce, plan_shared_prefix, read_probe,
+                  reshape_and_cache)
 
 __version__ = "0.1.0"

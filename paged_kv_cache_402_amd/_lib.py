@@ -71,10 +71,12 @@ SIGNATURES = {
                                                   c_int, c_int, c_int, c_int, c_float, c_int,
                                                   c_void_p, c_int, c_int, c_void_p, c_int,
                                                   c_void_p, c_size_t, c_void_p]),
-    "pkv_paged_attention_prefix": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p,
-                                           c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
-                                           c_int, c_float, c_int, c_void_p, c_int, c_int,
-                                           c_void_p, c_size_t, c_void_p]),
+    "pkv_paged_attention_prefix": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                           c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                           c_int, c_int, c_int, c_float, c_int, c_void_p, c_int,
+                                           c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_read_probe": (c_int, [c_void_p, c_size_t, c_int, c_void_p, c_int, c_int,
+                               ctypes.c_uint32, c_void_p, c_void_p]),
     "pkv_reshape_and_cache": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                       c_int, c_int, c_int, c_int, c_int, c_void_p]),
     "pkv_copy_blocks": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,

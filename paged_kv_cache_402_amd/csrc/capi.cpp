@@ -93,6 +93,7 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
     return fail(PKV_EINVAL, "decode: q and caches must be 16-byte aligned");
   const WsLayout ws = ws_layout(num_seqs, num_q_heads, pmax, head_dim);
   const size_t need = ws.total;
+  pl->ws_needed = need;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "decode: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need > 0 && !aligned16(workspace))
@@ -558,6 +559,9 @@ static int prefix_pass(const DecodePlan& pl, int kv_dtype, int head_dim, int blo
   if ((int64_t)d.num_kv_heads * ((num_members + per - 1) / per) > INT32_MAX)
     return fail(PKV_EINVAL, "prefix: too many members");
   PrefixArgs a;
+  a.out = d.out;
+  a.out_dtype = d.out_dtype;
+  a.seq_lens = d.seq_lens;
   a.q = d.q;
   a.k_cache = d.k_cache;
   a.v_cache = d.v_cache;
@@ -580,19 +584,18 @@ static int prefix_pass(const DecodePlan& pl, int kv_dtype, int head_dim, int blo
                     "shared-prefix launch");
 }
 
-int pkv_paged_attention_prefix(const void* q, const void* k_cache, const void* v_cache,
-                               int kv_dtype, const int32_t* block_tables, const int32_t* seq_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int num_blocks, int max_blocks_per_seq,
-                               float scale, int partition_size, const int32_t* members,
-                               int num_members, int prefix_partitions, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+int pkv_paged_attention_prefix(void* out, int out_dtype, const void* q, const void* k_cache,
+                               const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                               const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, float scale, int partition_size,
+                               const int32_t* members, int num_members, int prefix_partitions,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   DecodePlan pl;
-  // out is not written by this pass; q stands in for it in the shared argument checks
-  int st = plan_decode(&pl, const_cast<void*>(q), kv_dtype, q, k_cache, v_cache, kv_dtype,
-                       block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                       block_size, num_blocks, max_blocks_per_seq, scale, partition_size,
-                       workspace, workspace_bytes);
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables,
+                       seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, scale, partition_size, workspace,
+                       workspace_bytes);
   if (st != PKV_OK || num_seqs == 0) return st;
   return prefix_pass(pl, kv_dtype, head_dim, block_size, members, num_members, prefix_partitions,
                      stream);
@@ -673,6 +676,29 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                   "decode partitions launch");
   if (st != PKV_OK || pl.args.pmax <= 1) return st;
   return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
+                   int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
+                   void* stream) {
+  if (!is_pow2(tile_bytes) || tile_bytes < 256 || tile_bytes > (1 << 20))
+    return fail(PKV_EINVAL, "read_probe: tile_bytes must be a power of two in [256, 1 MiB]");
+  if (num_tiles < 0 || tiles_per_group < 1 || tiles_per_group > 1024)
+    return fail(PKV_EINVAL, "read_probe: num_tiles >= 0 and tiles_per_group in [1, 1024]");
+  if (num_tiles == 0) return ok();
+  if (!buf || !tile_ids || !sink) return fail(PKV_EINVAL, "read_probe: null pointer");
+  if (!aligned16(buf)) return fail(PKV_EINVAL, "read_probe: buffer must be 16-byte aligned");
+  if (buf_bytes < (size_t)tile_bytes) return fail(PKV_EINVAL, "read_probe: buffer holds no tile");
+  ProbeArgs a;
+  a.buf = static_cast<const unsigned char*>(buf);
+  a.tile_ids = tile_ids;
+  a.num_tile_slots = (int64_t)(buf_bytes / (size_t)tile_bytes);
+  a.num_tiles = num_tiles;
+  a.tiles_per_group = tiles_per_group;
+  a.tile_log2 = log2i(tile_bytes);
+  a.sentinel = sentinel;
+  a.sink = sink;
+  return hip_status(launch_read_probe(a, (hipStream_t)stream), "read probe launch");
 }
 
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache, int dtype,

@@ -95,6 +95,17 @@ template <> __device__ __forceinline__ uint32_t narrow_bits<BF16>(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Stores one output element of dtype out_dtype (fp32, or rounded to nearest-even 16 bits).
+__device__ __forceinline__ void store_out(void* out, size_t idx, float y, int out_dtype) {
+  if (out_dtype == F32) {
+    reinterpret_cast<float*>(out)[idx] = y;
+  } else if (out_dtype == BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)narrow_bits<BF16>(y);
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)narrow_bits<F16>(y);
+  }
+}
+
 // DPP lane permutations inside a row of 16 lanes (gfx9 encodings).
 enum : int {
   DPP_XOR1 = 0xB1,         // quad_perm [1,0,3,2]

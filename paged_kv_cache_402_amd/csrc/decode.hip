@@ -121,16 +121,6 @@ template <int N> __device__ __forceinline__ void lds_load_n(const float* src, fl
   }
 }
 
-__device__ __forceinline__ void store_out(void* out, size_t idx, float y, int out_dtype) {
-  if (out_dtype == F32) {
-    reinterpret_cast<float*>(out)[idx] = y;
-  } else if (out_dtype == BF16) {
-    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)narrow_bits<BF16>(y);
-  } else {
-    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)narrow_bits<F16>(y);
-  }
-}
-
 template <int DT, int D, int G, bool MF>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
   using K = Cfg<DT, D, G>;

@@ -58,10 +58,13 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t s
 // sequence list the same physical blocks; one workgroup per (KV head, 64 query rows of the
 // members, partition) writes the members' partials for those partitions.
 struct PrefixArgs {
+  void* out;                   // [B][Hq][D] of out_dtype: rows of single-partition members
+  int out_dtype;
   const void* q;               // [B][Hq][D]
   const void* k_cache;         // [NB][Hkv][bs][D]
   const void* v_cache;
   const int32_t* block_tables; // [B][max_blocks]; the first member's row gives the blocks
+  const int32_t* seq_lens;     // [B]: each member attends only to its own tokens
   const int32_t* members;      // [num_members] sequence indices
   float* ws_ml;                // same layout as DecodeArgs
   float* ws_acc;
@@ -91,5 +94,16 @@ struct CopyBlocksArgs {
   int64_t block_bytes;      // bytes of one block of one cache (all heads, all slots)
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
+// Read-bandwidth probe (probe.hip).
+struct ProbeArgs {
+  const unsigned char* buf;
+  const int32_t* tile_ids;   // [num_tiles]
+  int64_t num_tile_slots;    // tiles the buffer holds; ids outside [0, slots) are skipped
+  int num_tiles, tiles_per_group, tile_log2;
+  uint32_t sentinel;
+  uint32_t* sink;
+};
+hipError_t launch_read_probe(const ProbeArgs& a, hipStream_t stream);
 
 }  // namespace pkv

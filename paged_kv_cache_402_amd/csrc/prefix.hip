@@ -130,15 +130,30 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
       qv[j] = valid ? load16(qrow + (32 * j + 8 * g) * 2) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- the partition's block ids (from the first member's table) ----
+  // ---- the member's length, clamped as the per-partition kernel clamps it: the row attends
+  // only to tokens before it, so a member that ends inside a shared partition still gets
+  // exact partials (and its output row, when it has one partition only) ----
+  const int cap = a.max_blocks << a.bs_log2;
+  int Lr = valid ? a.seq_lens[b] : 0;
+  Lr = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
+  const int nrow = Lr - p * a.part;        // tokens of this partition the row attends to
+
+  // ---- the partition's block ids (from the first member's table); an entry outside the
+  // pool is kept as -1: its tokens are left out (as the per-partition kernel leaves them
+  // out), and its loads read block 0, which is inside the pool ----
   const int nblk = a.part >> a.bs_log2;
   const int32_t* trow = a.block_tables + (size_t)rep * a.max_blocks +
                         (((size_t)p * a.part) >> a.bs_log2);
+  int bad = 0;
   for (int i = tid; i < nblk; i += 256) {
     const int id = trow[i];
-    s_ids[i] = (unsigned)id < (unsigned)a.num_blocks ? id : 0;   // never read outside the pool
+    const bool in_pool = (unsigned)id < (unsigned)a.num_blocks;
+    s_ids[i] = in_pool ? id : -1;
+    bad |= !in_pool;
   }
-  __syncthreads();
+  const bool any_bad = __syncthreads_or(bad) != 0;
+  // per-token masking only in waves that need it (the usual shared prefix needs none)
+  const bool need_mask = any_bad || __builtin_amdgcn_ballot_w64(nrow < a.part) != 0;
 
   const int bs_mask = (1 << a.bs_log2) - 1;
   const size_t head_bytes = (size_t)kRow << a.bs_log2;       // one (block, head) tile
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
   const unsigned char* kbase = (const unsigned char*)a.k_cache + kvh * head_bytes;
   const unsigned char* vbase = (const unsigned char*)a.v_cache + kvh * head_bytes;
   auto row_off = [&](int tok) -> size_t {                     // partition-relative token
-    const int blk = s_ids[tok >> a.bs_log2];
+    const int blk = max(s_ids[tok >> a.bs_log2], 0);
     return (size_t)blk * block_bytes + (size_t)(tok & bs_mask) * kRow;
   };
 
@@ -183,8 +198,8 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one step of math on the staged tiles of buffer buf
-  auto compute = [&](int buf) {
+  // one step (the step-th 32 tokens of the partition) of math on the staged tiles of buffer buf
+  auto compute = [&](int buf, int step) {
     // every LDS operand of the step first (K: 8 x 16 B, V^T: 16 x 8 B), so their latencies
     // overlap one another and the products instead of being paid one read at a time
     const unsigned char* kt = s_k[buf] + (size_t)r * kKStride + 16 * g;
@@ -214,6 +229,17 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * hh + i] = c[i] * a.scale_log2;
     }
+    if (need_mask) {
+      // tokens 16 hh + 4 g + i of the step: the four share one block (blocks hold >= 8)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int tok = step * 32 + 16 * hh + 4 * g;
+        const bool blk_ok = !any_bad || s_ids[tok >> a.bs_log2] >= 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * hh + i] = blk_ok && tok + i < nrow ? sc[4 * hh + i] : -INFINITY;
+      }
+    }
     float mx = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
@@ -231,11 +257,14 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
     }
     uint32_t ph[4], pl[4];
     float psum = 0.f;
+    // the reference is -inf only while every token of the row so far was left out; then
+    // every score is -inf too, and a base of 0 gives them weight 0
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       // sc - m_run <= 8: the weights stay below 2^8; those under 2^-126 flush to zero
-      const float p0 = __builtin_amdgcn_exp2f(sc[e] - m_run);
-      const float p1 = __builtin_amdgcn_exp2f(sc[e + 1] - m_run);
+      const float p0 = __builtin_amdgcn_exp2f(sc[e] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(sc[e + 1] - mref);
       psum += p0 + p1;
       split_pair<DT>(p0, p1, ph[e >> 1], pl[e >> 1]);
     }
@@ -263,12 +292,25 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
       store_step(s & 1, ring[u]);
       load_step(min(s + PF, steps - 1), ring[u]);
       __syncthreads();
-      compute(s & 1);
+      compute(s & 1, s);
     }
   }
 
   const float l_row = xor_sum_from<16>(l_run);
   if (!valid) return;
+  const int nparts = Lr == 0 ? 1 : (Lr + a.part - 1) / a.part;
+  if (p >= nparts) return;                 // past the member's end: the merge never reads it
+  if (nparts == 1) {
+    // the member fits this (first) partition: no merge runs for it, so its row is final here
+    // (a member of length 0 gets a zero row)
+    const size_t o = ((size_t)b * a.num_q_heads + h) * kD + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_out(a.out, o + 16 * t + i, l_row > 0.f ? acc[t][i] / l_row : 0.f, a.out_dtype);
+    return;
+  }
   const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + p;
   float* dst = a.ws_acc + slot * kD + 4 * g;
 #pragma unroll

@@ -334,24 +334,22 @@ def paged_attention_partitions_step(out, q, k_new, v_new, cow_src, k_cache, v_ca
     return ws
 
 
-def paged_attention_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, members,
+def paged_attention_prefix(out, q, k_cache, v_cache, block_tables, seq_lens, scale, members,
                            prefix_partitions: int, workspace,
                            partition_size: int = DEFAULT_PARTITION):
     """The shared-prefix pass alone: writes the members' partials of the shared partitions
-    into `workspace` (as sized by decode_workspace_bytes)."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (workspace, "workspace")):
-        _dev(t, n)
-    _i32(block_tables, "block_tables")
-    _i32(seq_lens, "seq_lens")
+    into `workspace` (as sized by decode_workspace_bytes), and the output row of any member
+    that fits one partition into `out`."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    _dev(workspace, "workspace")
     _i32(members, "members")
-    B, Hq, D = q.shape
-    NB, Hkv, bs, _ = k_cache.shape
     check(lib.pkv_paged_attention_prefix(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), _kv_dtype(k_cache, "k_cache"),
-        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB,
-        block_tables.shape[1], float(scale), partition_size, members.data_ptr(),
-        members.shape[0], int(prefix_partitions), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(q)), "paged_attention_prefix")
+        out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
+        block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
+        partition_size, members.data_ptr(), members.shape[0], int(prefix_partitions),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)),
+        "paged_attention_prefix")
 
 
 def paged_attention_reduce(out, seq_lens, block_size, max_blocks_per_seq, workspace,
@@ -407,3 +405,16 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
                               _kv_dtype(k_cache, "k_cache"), src_dst_pairs.data_ptr(),
                               src_dst_pairs.shape[0], Hkv, D, bs, NB, _stream(k_cache)),
           "copy_blocks")
+
+
+def read_probe(buf, tile_bytes: int, tile_ids, tiles_per_group: int, sink, sentinel: int = 0x9E3779B9):
+    """Measurement only: reads the tile_bytes tiles of the byte buffer `buf` named by the
+    device int32 `tile_ids`, tiles_per_group of them per 256-lane workgroup (pkv_read_probe).
+    `sink` is a device int32/uint32 tensor of at least one element."""
+    _dev(buf, "buf")
+    _i32(tile_ids, "tile_ids")
+    _dev(sink, "sink")
+    check(lib.pkv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(tile_bytes),
+                             tile_ids.data_ptr(), tile_ids.numel(), int(tiles_per_group),
+                             int(sentinel) & 0xFFFFFFFF, sink.data_ptr(), _stream(buf)),
+          "read_probe")

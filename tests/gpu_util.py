@@ -65,6 +65,21 @@ def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
     return 2.0 ** (e - mant)
 
 
+def out_gate(ref: np.ndarray, kv_dtype: str, out_dtype) -> np.ndarray:
+    """Per-element max-abs-error gate for an output of out_dtype (None or "f32": fp32).
+
+    fp32 output: GATE[kv_dtype]. A 16-bit output is the fp32 result rounded once, to nearest,
+    which alone can move it by half an ulp: 1.95e-3 for bf16 |x| in [0.5, 1) and 3.9e-3 in
+    [1, 2). The gate is max(GATE[kv_dtype], half_ulp(|ref|) + 1e-5): the 2e-3 bar of 16-bit KV
+    wherever one rounding fits inside it (bf16 |x| < 1, fp16 |x| < 8), and otherwise half an
+    ulp plus the 1e-5 that the fp32 arithmetic before the rounding is held to (its fp32-KV
+    bar), so a value that lands next to a rounding midpoint still passes while a second
+    rounding or a wrong digit does not. Never looser than 2e-3."""
+    if out_dtype is None or out_dtype == "f32":
+        return np.full(np.shape(ref), GATE[kv_dtype])
+    return np.maximum(GATE[kv_dtype], half_ulp(ref, out_dtype) + GATE["f32"])
+
+
 def max_err(got, ref, rows=None):
     if rows is not None:
         got, ref = got[rows], ref[rows]

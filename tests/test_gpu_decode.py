@@ -6,8 +6,9 @@ Pages cited:
   P3 = aiknowledge.cn "2.2 PagedAttention 与 KV Cache 分页管理"
 
 Gates: max |HIP - oracle| <= 1e-5 (fp32 KV) or 2e-3 (fp16/bf16 KV) with fp32 output; with a
-16-bit output, the gate adds half an ulp of the output format at |oracle| (the rounding of the
-result itself). Pools hold NaN in every slot no sequence may read, so any stray read shows.
+16-bit output, max(2e-3, half an ulp of the output format at |oracle| + 1e-5), which is 2e-3
+wherever one rounding of the result fits inside it (tests/gpu_util.py: out_gate). Pools hold
+NaN in every slot no sequence may read, so any stray read shows.
 """
 import math
 
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 from workloads import gen
-from tests.gpu_util import (GATE, half_ulp, i32, max_err, oracle, run_decode, to_dev, to_host,
+from tests.gpu_util import (GATE, i32, max_err, oracle, out_gate, run_decode, to_dev, to_host,
                             TORCH_DT)
 
 pytestmark = pytest.mark.gpu
@@ -34,10 +35,7 @@ def _check(case, partition_size=512, out_dtype=None, seqs=None, ref=None):
     ref = oracle(case, seqs=seqs) if ref is None else ref
     rows = slice(None) if seqs is None else list(seqs)
     err = np.abs(got[rows] - ref[rows])
-    if out_dtype is None or out_dtype == "f32":
-        gate = GATE[case.dtype]
-    else:
-        gate = GATE[case.dtype] + half_ulp(ref[rows], out_dtype)
+    gate = out_gate(ref[rows], case.dtype, out_dtype)
     assert np.isfinite(got[rows]).all()
     assert (err <= gate).all(), "max err %g" % float(err.max())
     return got, ref
@@ -229,14 +227,28 @@ def test_seq_lens_beyond_table_are_clamped():
 
 
 def test_invalid_table_entries_are_skipped_without_faulting():
+    """Table entries outside the pool are skipped with their tokens (the kernel never
+    addresses memory through them). Sequence 2 lists only valid blocks and must match the
+    oracle exactly as usual; sequences 0 and 1 must match the oracle over the tokens of their
+    valid blocks (attention is invariant to which tokens sit where, so dropping a logical block
+    is the same as a shorter table without it)."""
     rng = np.random.default_rng(8)
-    case = gen.make_case("bad", rng, [40, 40], 4, 4, 128, 16, "bf16")
+    case = gen.make_case("bad", rng, [40, 40, 40], 4, 4, 128, 16, "bf16")
     bad = case.block_tables.copy()
     bad[0, 1] = case.num_blocks + 5     # out of the pool
     bad[1, 0] = -7
     got, _ = run_decode(case, tables=i32(bad))
-    # rows of sequences that only reference valid blocks are unaffected; the others are finite
     assert np.isfinite(got).all()
+    ref = oracle(case)
+    assert max_err(got[2], ref[2]) <= GATE["bf16"]
+    kept = np.full_like(case.block_tables, -1)
+    kept[0, :2] = case.block_tables[0, [0, 2]]    # 16 + 8 tokens
+    kept[1, :2] = case.block_tables[1, [1, 2]]
+    kept[2] = case.block_tables[2]
+    short = gen.PagedDecodeCase(**{**case.__dict__, "block_tables": kept,
+                                   "seq_lens": np.array([24, 24, 40], np.int32)})
+    ref_kept = oracle(short)
+    assert max_err(got[:2], ref_kept[:2]) <= GATE["bf16"]
 
 
 def test_scale_zero_gives_mean_of_values():
@@ -372,13 +384,15 @@ def _sampled_reference(case, q, k, v, seqs):
     return oracle(sub)
 
 
-@pytest.mark.parametrize("form", ["bench", "grid512"])
+@pytest.mark.parametrize("form", ["bench", "bench_f32out", "grid512"])
 @pytest.mark.parametrize("which", ["llama2_7b_mha", "llama3_8b_gqa_prefix", "long_context_splitk"])
 def test_full_size_sampled(which, form):
-    """form "bench" is the benchmark's launch: the default partition for the shapes, the host
-    work list, and every sequence's newest K/V row (fresh values) stored by the decode pass
-    itself; the reference reads the caches the pass leaves. "grid512": the one-call decode
-    over the full grid at 512-token partitions."""
+    """form "bench" is the benchmark's launch exactly as timed: the default partition for the
+    shapes, the host work list, every sequence's newest K/V row (fresh values) stored by the
+    per-partition pass itself, then the merge as its own launch, into an output of the KV
+    dtype; the reference reads the caches the pass leaves. "bench_f32out": the same launches
+    into an fp32 output (the arithmetic before the final rounding). "grid512": the one-call
+    decode over the full grid at 512-token partitions."""
     import paged_kv_cache_402_amd as pk
     maker = gen.WORKLOADS[which]
     case = maker(values=False)
@@ -392,12 +406,17 @@ def test_full_size_sampled(which, form):
         work = i32(pk.decode_work_list(case.seq_lens, W, bs, part))
         k_new = gen.device_normal((B, Hkv, D), dt, 4030, "cuda")
         v_new = gen.device_normal((B, Hkv, D), dt, 4031, "cuda")
-        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-        pk.paged_attention_decode_append(out, q, k_new, v_new, k, v, i32(case.block_tables),
-                                         i32(case.seq_lens), case.scale, partition_size=part,
-                                         work_list=work)
+        odt = TORCH_DT[dt] if form == "bench" else torch.float32
+        out = torch.full((B, Hq, D), float("nan"), dtype=odt, device="cuda")
+        tables, lens_d = i32(case.block_tables), i32(case.seq_lens)
+        ws = torch.empty(max(1, pk.decode_workspace_bytes(B, Hq, W, bs, D, part)),
+                         dtype=torch.uint8, device="cuda")
+        pk.paged_attention_partitions_append(out, q, k_new, v_new, k, v, tables, lens_d,
+                                             case.scale, partition_size=part, workspace=ws,
+                                             work_list=work)
+        pk.paged_attention_reduce(out, lens_d, bs, W, ws, partition_size=part)
         torch.cuda.synchronize()
-        got = out.cpu().numpy().astype(np.float64)
+        got = out.float().cpu().numpy().astype(np.float64)
         # the new rows sit where each table puts token L - 1
         lens = case.seq_lens.astype(np.int64)
         blk = torch.from_numpy(case.block_tables[np.arange(B), (lens - 1) // bs].astype(np.int64))
@@ -413,8 +432,12 @@ def test_full_size_sampled(which, form):
     # always include the longest and the shortest sequence
     seqs = sorted(set(seqs) | {int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))})
     ref = _sampled_reference(case, q, k, v, seqs)
+    odt = case.dtype if form == "bench" else None
     for r, s in enumerate(seqs):
-        assert max_err(got[s], ref[r]) <= GATE[case.dtype], "seq %d" % s
+        assert (np.abs(got[s] - ref[r]) <= out_gate(ref[r], case.dtype, odt)).all(), "seq %d" % s
+        if odt is not None:
+            # the benchmarked rows' magnitudes keep one bf16 rounding inside the 2e-3 bar
+            assert max_err(got[s], ref[r]) <= GATE[case.dtype], "seq %d" % s
 
 
 # --------------------------------------------------------------------------------------------
@@ -630,7 +653,7 @@ def test_packed_work_list_long_tail_full_size_sampled():
                   | {int(x) for x in rng.choice(128, 5, replace=False)})
     ref = _sampled_reference(case, q, k, v, seqs)
     for r, s_ in enumerate(seqs):
-        gate = GATE["f16"] + half_ulp(ref[r], "f16")
+        gate = out_gate(ref[r], "f16", "f16")
         assert (np.abs(got[s_] - ref[r]) <= gate).all(), "seq %d" % s_
 
 
@@ -777,7 +800,7 @@ def test_shared_prefix_with_fused_append():
     out = torch.full_like(plain, float("nan"))
     ws = torch.empty(pk.decode_workspace_bytes(B, hq, W, bs, 128, part), dtype=torch.uint8,
                      device="cuda")
-    pk.paged_attention_prefix(q, k2, v2, tables, lns, case.scale, i32(mem), pp, ws,
+    pk.paged_attention_prefix(out, q, k2, v2, tables, lns, case.scale, i32(mem), pp, ws,
                               partition_size=part)
     pk.paged_attention_partitions_append(out, q, kn, vn, k2, v2, tables, lns, case.scale,
                                          partition_size=part, workspace=ws, work_list=i32(items))
@@ -790,6 +813,62 @@ def test_shared_prefix_with_fused_append():
                               case.block_tables, case.scale, q=case.q,
                               k_cache=to_host(k2, dtype), v_cache=to_host(v2, dtype))
     assert max_err(out.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_shared_prefix_skips_out_of_pool_entries_and_short_members(dtype):
+    """The shared-prefix pass follows the per-partition kernel's rules for inputs the planner
+    never produces: a shared table entry outside the pool is left out with its tokens, and
+    every member attends only to its own tokens. Members here end inside the second shared
+    partition (300), inside the first (100: one partition, so the pass writes its row), exactly
+    at a partition end (256) and at 0 tokens (zero row). The reference is the oracle over the
+    same tables with the out-of-pool logical block taken out (attention does not depend on
+    which positions the remaining tokens hold)."""
+    import paged_kv_cache_402_amd as pk
+    hq, hkv, bs, part, share, n = 32, 8, 16, 256, 512, 9
+    rng = np.random.default_rng(57)
+    lens = [int(x) for x in rng.integers(share + 1, share + 900, size=n)]
+    lens += [300, 100, 256, 0, 400]          # four short members, then one non-member
+    members = list(range(n + 4))
+    case = _share_case("shbad", 58, lens, hq, hkv, bs, dtype, share, members)
+    B, W, NB = len(lens), case.block_tables.shape[1], case.num_blocks
+    bad_col = 5                              # tokens 80..95, inside every member but the last
+    tables = case.block_tables.copy()
+    for b in members:
+        tables[b, bad_col] = NB + 3
+    pp = share // part
+    items = []
+    for b, L in enumerate(lens):
+        npart = max(1, -(-L // part))
+        first = pp if b in members else 0
+        items += [(b << 16) | p for p in range(first, npart)]
+    dt = case.dtype
+    q, k, v = to_dev(case.q, dt), to_dev(case.k_cache, dt), to_dev(case.v_cache, dt)
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    pk.paged_attention_decode(out, q, k, v, i32(tables), i32(case.seq_lens), case.scale,
+                              partition_size=part, work_list=i32(np.array(items, np.uint32)
+                                                                  .view(np.int32)),
+                              shared_prefix=(i32(members), pp))
+    plain = torch.full_like(out, float("nan"))
+    pk.paged_attention_decode(plain, q, k, v, i32(tables), i32(case.seq_lens), case.scale,
+                              partition_size=part)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert (got[n + 3] == 0).all()                        # the 0-token member
+    kept = np.full_like(tables, -1)
+    kept_lens = case.seq_lens.copy()
+    for b in range(B):
+        row = case.block_tables[b].tolist()
+        if b in members and lens[b] > bad_col * bs:
+            assert lens[b] >= (bad_col + 1) * bs       # the left-out block is a full one
+            row = row[:bad_col] + row[bad_col + 1:] + [-1]
+            kept_lens[b] -= bs
+        kept[b] = row
+    ref = oracle(gen.PagedDecodeCase(**{**case.__dict__, "block_tables": kept,
+                                        "seq_lens": kept_lens}))
+    assert max_err(got, ref) <= GATE[dtype]
+    assert max_err(got, plain.cpu().numpy().astype(np.float64)) <= 1e-4
 
 
 @pytest.mark.parametrize("seed", range(16))
