@@ -116,6 +116,26 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                int max_blocks_per_seq, float scale, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same two launches
+ * and bitwise the same output, with the split-K partials in the library's own fixed scratch
+ * area (64 MiB, a file-scope device array; each GPU the library runs on holds one until the
+ * process ends) instead of a caller workspace. Nothing is allocated, by the library or
+ * anyone: the area's address on the current device is looked up once (hipGetSymbolAddress)
+ * at the first call on that device. Shapes whose partials need more than 64 MiB
+ * (pkv_decode_workspace_bytes > 64 MiB) fail with PKV_EWORKSPACE and launch nothing. Every
+ * call on one GPU uses the same area and nothing in it needs clearing (every partial the merge
+ * reads is written first by the same call), so calls on one GPU must not overlap in time:
+ * calls on different streams, or from different threads, without ordering between them
+ * race. */
+int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q,
+                                       const void* k_cache, const void* v_cache, int kv_dtype,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       int max_blocks_per_seq, float scale, int partition_size,
+                                       void* stream);
+
 /* The two launches of pkv_paged_attention_decode, exposed separately so a caller can time or
  * schedule them apart. Same arguments and results as the combined call:
  *   _partitions: one workgroup per (KV head, sequence, partition) attends over its partition;

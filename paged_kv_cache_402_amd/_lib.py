@@ -23,6 +23,10 @@ SIGNATURES = {
                                            c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_float, c_int, c_void_p, c_size_t,
                                            c_void_p]),
+    "pkv_paged_attention_decode_noalloc": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
+                                                   c_void_p, c_int, c_void_p, c_void_p, c_int,
+                                                   c_int, c_int, c_int, c_int, c_int, c_int,
+                                                   c_float, c_int, c_void_p]),
     "pkv_paged_attention_partitions": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                c_int, c_int, c_int, c_int, c_float, c_int,

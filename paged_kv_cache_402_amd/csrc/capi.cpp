@@ -678,6 +678,31 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
   return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
 }
 
+int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q,
+                                       const void* k_cache, const void* v_cache, int kv_dtype,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       int max_blocks_per_seq, float scale, int partition_size,
+                                       void* stream) {
+  void* ws = nullptr;
+  int st = hip_status(static_workspace(&ws), "decode_noalloc: static scratch address");
+  if (st != PKV_OK) return st;
+  DecodePlan pl;
+  st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                   num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, scale, partition_size, ws, kStaticWorkspaceBytes);
+  if (st == PKV_EWORKSPACE)
+    return fail(PKV_EWORKSPACE, "decode_noalloc: these shapes need %zu bytes of split-K scratch; "
+                "the static area holds %zu (use pkv_paged_attention_decode with a workspace, "
+                "or longer partitions)", pl.ws_needed, kStaticWorkspaceBytes);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
+                  "decode partitions launch");
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
 int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
                    int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
                    void* stream) {

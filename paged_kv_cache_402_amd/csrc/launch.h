@@ -95,6 +95,11 @@ struct CopyBlocksArgs {
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
+// Split-K scratch of the allocation-free decode (static_ws.hip): a file-scope device array of
+// kStaticWorkspaceBytes per device; *ptr receives its address on the current device.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+hipError_t static_workspace(void** ptr);
+
 // Read-bandwidth probe (probe.hip).
 struct ProbeArgs {
   const unsigned char* buf;
