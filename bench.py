@@ -68,6 +68,10 @@ def parse_args():
                    help="only measure plain HBM reads (pkv_read_probe): a 2 GiB stream, random "
                         "tiles of 4-64 KiB from a 2.5 GiB pool, and the GQA 8B workload's "
                         "pattern with a block's 8 heads read by 8 workgroups or by one")
+    p.add_argument("--timeline", action="store_true",
+                   help="after the timed steps, run 3 more with the per-workgroup timeline of the "
+                        "decode partition kernel switched on (pkv_debug_timeline) and report "
+                        "ramp-up, occupancy, tail and per-workgroup fixed cost")
     p.add_argument("--no-read-probe", action="store_true",
                    help="leave the short read probe (achievable_GBps) out of the headline run")
     p.add_argument("--warm", action="store_true",
@@ -448,6 +452,64 @@ def read_probe(pk, torch, dev, full, reps=10):
     return res
 
 
+def timeline_summary(tl, items, num_kv_heads, part, lens, kv_row_bytes):
+    """Per-workgroup records {start, end, HW_ID, XCC_ID} (100 MHz clock) of one launch over
+    a work list -> occupancy, ramp-up, tail and fixed cost per workgroup."""
+    rec = tl.reshape(-1, 8).astype(np.int64)
+    ok = rec[:, 1] != 0
+    wg = np.nonzero(ok)[0]
+    unit = rec[ok, 4]
+    t0 = rec[ok, 0].min()
+    start = (rec[ok, 0] - t0) / 100.0          # us
+    end = (rec[ok, 1] - t0) / 100.0
+    span = float(end.max())
+    # tokens of each workgroup's partition
+    it = items[unit // num_kv_heads].astype(np.int64) & 0xFFFFFFFF
+    b, p = it >> 16, it & 0xFFFF
+    n = np.minimum(lens[b].astype(np.int64) - p * part, part)
+    grid = np.arange(0.0, span, 0.25)
+    active = np.array([int(((start <= t) & (end > t)).sum()) for t in grid])
+    peak = int(active.max())
+    ramp = float(grid[np.argmax(active >= 0.95 * peak)])
+    tail_from = float(grid[len(active) - 1 - np.argmax(active[::-1] >= 0.9 * peak)])
+    dur = end - start
+    # duration = fixed + per-token: least squares over all workgroups
+    A = np.stack([np.ones_like(n, dtype=np.float64), n.astype(np.float64)], 1)
+    coef = np.linalg.lstsq(A, dur, rcond=None)[0]
+    xcc = rec[ok, 3] & 0xF
+    first_k = float(np.sort(start)[min(len(start) - 1, peak - 1)])
+    head = unit % num_kv_heads
+    # bandwidth estimate: each workgroup's KV bytes (K and V rows of its tokens, one head)
+    # spread evenly over its lifetime, summed per 5 us window
+    kv_bytes = 2 * n.astype(np.float64) * kv_row_bytes
+    win = 5.0
+    edges = np.arange(0.0, span + win, win)
+    bw = np.zeros(len(edges) - 1)
+    for s0, e0, by in zip(start, end, kv_bytes):
+        if e0 <= s0:
+            continue
+        lo = np.clip(edges[:-1], s0, e0)
+        hi = np.clip(edges[1:], s0, e0)
+        bw += by * (hi - lo) / (e0 - s0)
+    bw_tbps = bw / (win * 1e-6) / 1e12
+    mean_bw = float(kv_bytes.sum() / (span * 1e-6) / 1e12)
+    return {"workgroups": int(ok.sum()), "span_us": round(span, 2), "peak_active": peak,
+            "xcd_is_id_mod_8": round(float(((wg % 8) == xcc).mean()), 4),
+            "last_end_per_head_us": [round(float(end[head == h].max()), 2)
+                                     for h in range(min(num_kv_heads, 8))],
+            "mean_active": round(float(active.mean()), 1),
+            "ramp_to_95pct_us": round(ramp, 2),
+            "first_%d_started_by_us" % peak: round(first_k, 2),
+            "tail_below_90pct_us": round(span - tail_from, 2),
+            "fixed_us_per_workgroup": round(float(coef[0]), 2),
+            "us_per_1k_tokens": round(float(coef[1]) * 1000, 2),
+            "mean_duration_us": round(float(dur.mean()), 2),
+            "last_end_per_xcd_us": [round(float(end[xcc == x].max()), 2) if (xcc == x).any()
+                                    else None for x in range(8)],
+            "kv_TBps_mean": round(mean_bw, 3),
+            "kv_TBps_per_5us": [round(float(x), 2) for x in bw_tbps]}
+
+
 def serve_loop(pk, torch, dev, steps, static=False, warm_steps=None):
     """Continuous batching on synthetic traffic with the GQA 8B layer shape (32 query / 8 KV
     heads, head_dim 128, block 16, bf16): Poisson arrivals of 2.5 requests per step, prompts
@@ -716,6 +778,8 @@ def main():
     ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
                                          case.block_size, case.head_dim, part)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    if ws_bytes:
+        pk.decode_workspace_init(ws)     # list launches hand out late units from its header
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
@@ -739,8 +803,6 @@ def main():
         ([] if fused else ["reshape_and_cache"]) + \
         (["shared_prefix"] if members is not None and pp > 0 else []) + \
         ["decode_partitions"] + (["partition_reduce"] if ws_bytes > 0 else [])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(K)]
 
     def run_stage(name):
         if name == "copy_blocks":
@@ -769,13 +831,20 @@ def main():
             pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width,
                                       ws, partition_size=part)
 
-    def step(i=None):
-        if i is not None:
-            ev[i][0].record()
+    def step(evs=None):
+        """One step; evs: None, or events recorded before the first stage and after the last
+        (two events), or before the first and after every stage (len(stages) + 1)."""
+        if evs is not None:
+            evs[0].record()
         for j, name in enumerate(stages):
             run_stage(name)
-            if i is not None:
-                ev[i][j + 1].record()
+            if evs is not None and len(evs) > 2:
+                evs[j + 1].record()
+        if evs is not None and len(evs) == 2:
+            evs[1].record()
+
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
     log("warmup %d" % W)
     for _ in range(W):
@@ -787,31 +856,43 @@ def main():
     # every step gives the step the same cold L2 and memory-side cache.
     evict = None if args.warm else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     evict_sum = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def timed(nev):
+        """K steps (each after the eviction read unless --warm); returns (events per step,
+        wall ms per step)."""
+        ev = [new_events(nev) for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            if evict is not None:
+                torch.sum(evict, dim=0, out=evict_sum)
+            step(ev[i])
+        torch.cuda.synchronize()
+        return ev, (time.perf_counter() - t0) * 1e3 / K
+
+    # The step: two events per step, around its whole launch sequence, so nothing is
+    # recorded between its kernels. Cold: the step's own span (the eviction sits before it).
     log("timing %d steps%s" % (K, "" if args.warm else " (1 GiB read before each)"))
-    t0 = time.perf_counter()
-    for i in range(K):
-        if evict is not None:
-            torch.sum(evict, dim=0, out=evict_sum)
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_wall = (t1 - t0) * 1e3 / K
-    # cold: the step's own span between its first and last event (the eviction sits before it)
-    step_ms = np.array([e[0].elapsed_time(e[-1]) for e in ev])
+    ev, ms_wall = timed(2)
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     ms_step = ms_wall if args.warm else float(np.mean(step_ms))
-    per = {name: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, name in enumerate(stages)}
+    # The breakdown and the decode kernel's launch duration (roofline): K more steps, with an
+    # event after every stage.
+    log("timing %d steps with an event after every stage" % K)
+    ev_st, _ = timed(len(stages) + 1)
+    ms_step_staged = float(np.mean([e[0].elapsed_time(e[-1]) for e in ev_st]))
+    per = {name: [e[j].elapsed_time(e[j + 1]) for e in ev_st] for j, name in enumerate(stages)}
     stage_ms = {name: round(float(np.mean(per[name])), 5) if name in per else None
                 for name in ("decode_partitions", "partition_reduce", "copy_blocks",
                              "reshape_and_cache", "shared_prefix")}
     t_dec = per["decode_partitions"]
-    t_red = stage_ms["partition_reduce"]
-    t_cw = stage_ms["reshape_and_cache"]
     dec_ms = float(np.mean(t_dec))
     gbps = bytes_["kv_unique"] / (ms_step * 1e-3) / 1e9
     kernel_bytes = bytes_["decode_kernel"]
     achieved = kernel_bytes / (dec_ms * 1e-3) / 1e9
-    log("step %.4f ms, decode kernel %.4f ms (p10 %.4f, p90 %.4f); %s"
-        % (ms_step, dec_ms, np.percentile(t_dec, 10), np.percentile(t_dec, 90),
+    log("step %.4f ms (median %.4f; %.4f with an event after every stage), decode kernel "
+        "%.4f ms (p10 %.4f, p90 %.4f); %s"
+        % (ms_step, float(np.median(step_ms)), ms_step_staged, dec_ms,
+           np.percentile(t_dec, 10), np.percentile(t_dec, 90),
            ", ".join("%s %.4f ms" % (k, v) for k, v in stage_ms.items()
                      if v is not None and k != "decode_partitions")))
 
@@ -827,9 +908,11 @@ def main():
         "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 5),
                                 round(float(np.percentile(step_ms, 90)), 5)],
         "timing": "wall clock over back-to-back steps (warm caches)" if args.warm else
-                  ("HIP events around each step, 1 GiB read before each (cold L2 and "
-                   "memory-side cache); wall clock incl. the eviction reads %.4f ms/step"
-                   % ms_wall),
+                  ("HIP events around each step's launches (none between them), 1 GiB read "
+                   "before each (cold L2 and memory-side cache); wall clock incl. the eviction "
+                   "reads %.4f ms/step. kernel_ms and roofline come from %d more steps with "
+                   "an event after every stage (step %.5f ms there)"
+                   % (ms_wall, K, ms_step_staged)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -876,8 +959,34 @@ def main():
                                      % HBM_PEAK_GBPS)
         result["frac_of_achievable"] = round(gbps / ach, 4)
         result["read_probe"] = probe
+    if args.timeline:
+        if work is None or isinstance(work, tuple):
+            raise SystemExit("--timeline needs the plain work list (--grid list, no --pack)")
+        from paged_kv_cache_402_amd._lib import lib as _plib
+        cap = case.num_kv_heads * int(work.shape[0])
+        tl = torch.zeros(8 * cap, dtype=torch.int32, device=dev)
+        summaries = []
+        for _ in range(3):
+            tl.zero_()
+            if evict is not None:
+                torch.sum(evict, dim=0, out=evict_sum)
+            torch.cuda.synchronize()
+            pk.check(_plib.pkv_debug_timeline(tl.data_ptr(), cap), "debug_timeline")
+            step()
+            torch.cuda.synchronize()
+            pk.check(_plib.pkv_debug_timeline(None, 0), "debug_timeline")
+            eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
+            summaries.append(timeline_summary(tl.cpu().numpy().view(np.uint32), work.cpu().numpy(),
+                                              case.num_kv_heads, part, case.seq_lens,
+                                              case.head_dim * eb))
+            log("timeline: %s" % summaries[-1])
+        result_timeline = summaries
+    else:
+        result_timeline = None
     log("host manager cost")
     result["host_manager_us_per_step"] = round(host_manager_cost(pk, case), 1)
+    if result_timeline is not None:
+        result["timeline"] = result_timeline
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, about %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds, gen)

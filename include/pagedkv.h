@@ -80,13 +80,24 @@ const char* pkv_last_error(void);
  * Device operations
  * ========================================================================================== */
 
-/* Bytes of split-K workspace pkv_paged_attention_decode needs: for every (sequence, query
- * head, context partition) one running max and one exponent sum (fp32 pairs, their area
- * padded to a multiple of 16 bytes), then one head_dim-long fp32 accumulator. partition_size
- * defaults to 512 when 0 is passed. Returns 0 on bad input or when no sequence can span two
- * partitions. */
+/* Bytes of split-K workspace pkv_paged_attention_decode needs: a 256-byte header (its first
+ * 8 bytes are the scheduling word below), then for every (sequence, query head, context
+ * partition) one running max and one exponent sum (fp32 pairs, their area padded to a
+ * multiple of 16 bytes), then one head_dim-long fp32 accumulator. partition_size defaults to
+ * 512 when 0 is passed. Returns 0 on bad input or when no sequence can span two partitions. */
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_per_seq,
                                   int block_size, int head_dim, int partition_size);
+
+/* Initialises a workspace's scheduling word (one tiny kernel on stream; no allocation, no
+ * memset). Optional: the per-partition pass over a work list (the _list, _append, _step and
+ * _shared entry points) then hands the work units of the workgroups that start after the
+ * first resident round out in the list's order from that word, one atomic per workgroup, so
+ * the last, short partitions go to whichever XCD has room instead of a fixed eighth of them to
+ * each; the output is bitwise the same either way. Each call leaves the word initialised, so
+ * once per workspace (for instance right after allocating it) is enough. A workspace that was
+ * never initialised works too, with the fixed assignment. Calls sharing a workspace must not
+ * overlap in time (already required by the partials). A workspace_bytes of 0 is a no-op. */
+int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode attention over the paged cache (P1 §4.2; P2 §3.1; P3 §2.2.4: the kernel reads
  * KV block by block through the block table).
@@ -368,6 +379,18 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int dtype, const int32_t* src_
 int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
                    int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
                    void* stream);
+
+/* Per-workgroup timeline of the per-partition decode pass (measurement only; no page defines
+ * it). With capacity > 0, every later launch of the per-partition pass (any decode entry
+ * point) writes, for each of its workgroups w < capacity, eight uint32 at buf + 8 w: start
+ * and end time (s_memrealtime, a 100 MHz clock, low 32 bits), the HW_ID register (CU, SIMD
+ * and shader-engine ids), the XCC_ID register (XCD), the work unit it took (work-list
+ * launches: row * num_kv_heads + KV head; else w) and three zeros, from the workgroup's first
+ * lane. Workgroups that find no work (list entries past a sequence's end) write nothing, so
+ * clear the buffer first. buf: device, 16-byte aligned, 32 * capacity bytes, owned by the
+ * caller and kept alive until the timeline is switched off with capacity 0. Process-wide;
+ * not for concurrent use with launches on other threads. */
+int pkv_debug_timeline(void* buf, int capacity);
 
 /* ==========================================================================================
  * Host block manager (P2 §3.1 manager sketch; P1 §4.1-§4.3, §6; P3 §2.2.2-§2.2.3)

@@ -7,12 +7,12 @@ The device operations run in hand-written HIP kernels for gfx950 inside libpaged
 include/pagedkv.h); the block manager is C++ in the same library. Importing fails loudly if the
 library has not been built (python paged_kv_cache_402_amd/build.py).
 """
-from ._lib import PagedKVError, lib, last_error  # noqa: F401  (raises if the library is missing)
+from ._lib import PagedKVError, check, lib, last_error  # noqa: F401  (raises if missing)
 from .block_manager import BlockManager  # noqa: F401
 from .scheduler import Scheduler  # noqa: F401
 from .pool_plan import kv_pool_plan  # noqa: F401
 from .ops import (copy_blocks, decode_work_list, decode_work_list_packed,  # noqa: F401
-                  decode_workspace_bytes,
+                  decode_workspace_bytes, decode_workspace_init,
                   default_partition,
                   paged_attention_decode, paged_attention_decode_append,
                   paged_attention_decode_step, paged_attention_partitions_step,

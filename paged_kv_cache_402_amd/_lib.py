@@ -19,6 +19,7 @@ SIGNATURES = {
     "pkv_version": (c_int, []),
     "pkv_last_error": (c_char_p, []),
     "pkv_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "pkv_decode_workspace_init": (c_int, [c_void_p, c_size_t, c_void_p]),
     "pkv_paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                            c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_float, c_int, c_void_p, c_size_t,
@@ -79,6 +80,7 @@ SIGNATURES = {
                                            c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_int, c_float, c_int, c_void_p, c_int,
                                            c_int, c_void_p, c_size_t, c_void_p]),
+    "pkv_debug_timeline": (c_int, [c_void_p, c_int]),
     "pkv_read_probe": (c_int, [c_void_p, c_size_t, c_int, c_void_p, c_int, c_int,
                                ctypes.c_uint32, c_void_p, c_void_p]),
     "pkv_reshape_and_cache": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,

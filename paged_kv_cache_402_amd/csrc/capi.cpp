@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -14,6 +15,16 @@
 #include "pagedkv.h"
 
 namespace pkv {
+
+namespace {
+std::atomic<uint32_t*> g_timeline{nullptr};
+std::atomic<int> g_timeline_cap{0};
+}  // namespace
+
+void decode_timeline(uint32_t** buf, int* cap) {
+  *cap = g_timeline_cap.load(std::memory_order_acquire);
+  *buf = *cap > 0 ? g_timeline.load(std::memory_order_acquire) : nullptr;
+}
 
 namespace {
 
@@ -36,17 +47,18 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Split-K workspace: (max, sum) floats [B][Hq][pmax][2], padded to a multiple of 16 bytes so
-// that the accumulators [B][Hq][pmax][D] floats after them take 16-byte loads. Nothing when no
-// sequence can span two partitions.
+// Split-K workspace: a 256-byte header (its first 8 bytes: the scheduling word of the
+// per-partition pass over a work list), then (max, sum) floats [B][Hq][pmax][2], padded to a
+// multiple of 16 bytes so that the accumulators [B][Hq][pmax][D] floats after them take
+// 16-byte loads. Nothing when no sequence can span two partitions.
 struct WsLayout {
-  size_t acc_off, total;
+  size_t ml_off, acc_off, total;
 };
 WsLayout ws_layout(int64_t num_seqs, int64_t num_q_heads, int64_t pmax, int64_t head_dim) {
-  if (pmax <= 1) return {0, 0};
+  if (pmax <= 1) return {0, 0, 0};
   const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)pmax;
   const size_t ml = (rows * 8 + 15) / 16 * 16;
-  return {ml, ml + rows * (size_t)head_dim * 4};
+  return {kWsHeaderBytes, kWsHeaderBytes + ml, kWsHeaderBytes + ml + rows * (size_t)head_dim * 4};
 }
 
 struct DecodePlan {
@@ -89,8 +101,8 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   if (pmax > kMaxGridYZ) return fail(PKV_EINVAL, "decode: too many partitions per sequence");
   if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens))
     return fail(PKV_EINVAL, "decode: null pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PKV_EINVAL, "decode: q and caches must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_EINVAL, "decode: out, q and caches must be 16-byte aligned");
   const WsLayout ws = ws_layout(num_seqs, num_q_heads, pmax, head_dim);
   const size_t need = ws.total;
   pl->ws_needed = need;
@@ -106,8 +118,10 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  a.ws_ml = reinterpret_cast<float*>(workspace);
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_off) : nullptr;
   a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_off) : nullptr;
+  a.sched = need ? reinterpret_cast<unsigned long long*>(workspace) : nullptr;
+  a.sched_static = 0;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -123,6 +137,7 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.k_new = nullptr;
   a.cow_src = nullptr;
   a.v_new = nullptr;
+  decode_timeline(&a.timeline, &a.timeline_cap);
   pl->group = group;
   pl->ws_needed = need;
   return ok();
@@ -646,11 +661,14 @@ int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens
     return fail(PKV_EWORKSPACE, "reduce: workspace of %zu bytes needed, %zu given", ws.total, workspace_bytes);
   if (!aligned16(workspace)) return fail(PKV_EINVAL, "reduce: workspace must be 16-byte aligned");
   if (!out || !seq_lens) return fail(PKV_EINVAL, "reduce: null pointer");
+  if (!aligned16(out)) return fail(PKV_EINVAL, "reduce: out must be 16-byte aligned");
   DecodeArgs a = {};
   a.out = out;
   a.seq_lens = seq_lens;
-  a.ws_ml = (float*)workspace;
+  a.ws_ml = (float*)((const char*)workspace + ws.ml_off);
   a.ws_acc = (float*)((const char*)workspace + ws.acc_off);
+  a.sched = nullptr;
+  a.sched_static = 0;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.max_blocks = max_blocks_per_seq;
@@ -701,6 +719,25 @@ int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q,
                   "decode partitions launch");
   if (st != PKV_OK || pl.args.pmax <= 1) return st;
   return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
+}
+
+int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return ok();
+  if (!workspace || workspace_bytes < kWsHeaderBytes)
+    return fail(PKV_EINVAL, "workspace_init: a workspace holds at least %zu bytes", kWsHeaderBytes);
+  if (!aligned16(workspace)) return fail(PKV_EINVAL, "workspace_init: workspace must be 16-byte aligned");
+  return hip_status(launch_sched_init(static_cast<unsigned long long*>(workspace), (hipStream_t)stream),
+                    "workspace init launch");
+}
+
+int pkv_debug_timeline(void* buf, int capacity) {
+  if (capacity < 0 || (capacity > 0 && !buf)) return fail(PKV_EINVAL, "debug_timeline: bad buffer");
+  if (capacity > 0 && (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
+    return fail(PKV_EINVAL, "debug_timeline: buffer must be 16-byte aligned");
+  g_timeline_cap.store(0, std::memory_order_release);
+  g_timeline.store(static_cast<uint32_t*>(buf), std::memory_order_release);
+  g_timeline_cap.store(capacity, std::memory_order_release);
+  return ok();
 }
 
 int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,

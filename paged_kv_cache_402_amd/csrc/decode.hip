@@ -45,6 +45,9 @@
 // The arithmetic order does not depend on where blocks sit in the pool.
 #include <math.h>
 
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "launch.h"
 
@@ -121,26 +124,75 @@ template <int N> __device__ __forceinline__ void lds_load_n(const float* src, fl
   }
 }
 
+// Work unit of a workgroup that starts after the first resident round of a work-list launch:
+// the next ticket of the scheduling word, in the list's order. Workgroups are dealt to the
+// XCDs round-robin in a fixed share, and XCDs run at slightly different speeds, so a static
+// unit per workgroup leaves the fast XCDs idle at the end of the launch; taken this way, the
+// units that remain when a workgroup starts go to it, wherever it runs, and the short last
+// partitions of the list fill in behind the long ones on every XCD. One atomic per such
+// workgroup, no waiting. A word that does not carry the cookie (a workspace that was never
+// initialised) leaves every workgroup its static unit.
+__device__ __forceinline__ unsigned take_unit(const DecodeArgs& a) {
+  const unsigned dyn = (unsigned)(a.work_items * a.num_kv_heads - a.sched_static);
+  const unsigned long long old = atomicAdd(a.sched, 1ull);
+  const unsigned ticket = (unsigned)old;
+  if ((unsigned)(old >> 32) != kSchedCookie || ticket >= dyn) return blockIdx.x;
+  if (ticket == dyn - 1) atomicExch(a.sched, (unsigned long long)kSchedCookie << 32);
+  return (unsigned)a.sched_static + ticket;
+}
+
+__global__ void sched_init_kernel(unsigned long long* sched) {
+  if (threadIdx.x == 0) *sched = (unsigned long long)kSchedCookie << 32;
+}
+
+hipError_t launch_sched_init(unsigned long long* sched, hipStream_t stream) {
+  hipLaunchKernelGGL(sched_init_kernel, dim3(1), dim3(64), 0, stream, sched);
+  return hipGetLastError();
+}
+
+// Measurement only: workgroup start and end (s_memrealtime, 100 MHz) and where it ran.
+__device__ __forceinline__ void record_timeline(const DecodeArgs& a, uint32_t t_start,
+                                                unsigned unit) {
+  if (a.timeline != nullptr && threadIdx.x == 0 && blockIdx.x < (unsigned)a.timeline_cap) {
+    const uint32_t t_end = (uint32_t)__builtin_amdgcn_s_memrealtime();
+    const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_REG_HW_ID
+    const uint32_t xcc_id = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // HW_REG_XCC_ID
+    uint32_t* rec = a.timeline + 8 * (size_t)blockIdx.x;
+    store16(rec, u32x4{t_start, t_end, hw_id, xcc_id});
+    store16(rec + 4, u32x4{unit, 0u, 0u, 0u});
+  }
+}
+
 template <int DT, int D, int G, bool MF>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
   using K = Cfg<DT, D, G>;
   constexpr int NW = kDecodeWaves;
   constexpr int NT = kDecodeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
+  const uint32_t t_start = a.timeline != nullptr ? (uint32_t)__builtin_amdgcn_s_memrealtime() : 0u;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int kvh, pi, b;
+  unsigned unit = blockIdx.x;   // work unit (list launches: row * Hkv + KV head)
   // packed row: the four waves take four short partitions (four items stored from index
   // idx of the list) of the same KV head, each on its own, with no merge between them
   bool packed = false;
   if (a.work != nullptr) {
-    // consecutive workgroups take the KV heads of one row, so with 8 KV heads each XCD of
-    // the round-robin dispatch keeps to one head
-    const unsigned item = blockIdx.x / (unsigned)a.num_kv_heads;
-    kvh = blockIdx.x - item * a.num_kv_heads;
+    // unit u is (row u / Hkv, KV head u % Hkv): consecutive units take the KV heads of one
+    // row, so with 8 KV heads each XCD of the round-robin dispatch keeps to one head for the
+    // first resident round (a prefix shared by many sequences stays in that XCD's L2); later
+    // workgroups take their units from the scheduling word when there is one
+    if (a.sched != nullptr && (int)blockIdx.x >= a.sched_static) {
+      __shared__ unsigned s_unit;
+      if (tid == 0) s_unit = take_unit(a);
+      __syncthreads();
+      unit = s_unit;
+    }
+    const unsigned item = unit / (unsigned)a.num_kv_heads;
+    kvh = unit - item * a.num_kv_heads;
     uint32_t w = a.work[item];
     if (w & kPackedRow) {
       packed = true;
@@ -511,6 +563,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       }
     }
     cow_copy();
+    record_timeline(a, t_start, unit);
     return;
   }
   // every lane's score reads are done before the area is reused (LDS keeps a wave's order)
@@ -562,6 +615,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
   }
   cow_copy();
+  record_timeline(a, t_start, unit);
 }
 
 // Merge of the partitions of one (sequence, query head):
@@ -645,22 +699,60 @@ size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
   return (size_t)kDecodeWaves * (size_t)per * (size_t)group * 4;
 }
 
+// Workgroups of `kernel` resident at once on the current device with `lds` bytes of dynamic
+// LDS (occupancy query, cached per kernel, LDS size and device); 0 if unknown.
+static int resident_groups(const void* kernel, size_t lds) {
+  struct Entry {
+    const void* kernel;
+    size_t lds;
+    int device, groups;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+      if (e.kernel == kernel && e.lds == lds && e.device == dev) return e.groups;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeThreads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int groups = per_cu * cus;
+  std::lock_guard<std::mutex> lock(mu);
+  cache.push_back({kernel, lds, dev, groups});
+  return groups;
+}
+
+template <int DT, int D, int G, bool MF>
+static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
+  const auto kernel = paged_decode_partition_kernel<DT, D, G, MF>;
+  if (a.work != nullptr) {
+    const int units = a.num_kv_heads * a.work_items;
+    // the first resident round keeps its static units; dynamic units only pay off after it
+    const int resident = a.sched != nullptr ? resident_groups((const void*)kernel, lds) : 0;
+    if (resident <= 0 || resident >= units) a.sched = nullptr;
+    a.sched_static = resident;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kDecodeThreads), lds, stream, a);
+  } else {
+    a.sched = nullptr;
+    hipLaunchKernelGGL(kernel, dim3(a.num_kv_heads, a.pmax, a.num_seqs), dim3(kDecodeThreads),
+                       lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int D, int G>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid = a.work != nullptr ? dim3((unsigned)a.num_kv_heads * (unsigned)a.work_items)
-                                       : dim3(a.num_kv_heads, a.pmax, a.num_seqs);
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
   // Matrix-core scores for 16-bit data at G = 8, when a 16-token step stays inside one block
   // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured
   // faster (the padded 16-row product does 4x the work there and the K pass is not the limit).
   constexpr bool kMF = DT != F32 && G == 8;
-  if (kMF && a.bs_log2 >= 4 && a.part % 64 == 0)
-    hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, kMF>), grid,
-                       dim3(kDecodeThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL((paged_decode_partition_kernel<DT, D, G, false>), grid,
-                       dim3(kDecodeThreads), lds, stream, a);
-  return hipGetLastError();
+  if (kMF && a.bs_log2 >= 4 && a.part % 64 == 0) return launch_k<DT, D, G, kMF>(a, lds, stream);
+  return launch_k<DT, D, G, false>(a, lds, stream);
 }
 
 template <int DT, int D>
@@ -696,83 +788,91 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_
   }
 }
 
-// The same merge with one wave per (sequence, query head), four rows per workgroup, for
-// sequences of a few partitions: D/4 lanes cover a row and 256/D slices of the wave take the
-// partitions in turn; the slices are combined with lane shuffles in a fixed tree (slice 0,
-// which writes the row, always computes the same expression). A quarter of the waves of the
-// 4-wave form, so a batch of short sequences merges in one round of the machine's wave slots.
+// The same merge for sequences of a few partitions, one workgroup per sequence for all its
+// query heads: D/16 lanes cover a head's row (16 columns each: four 16-byte loads per
+// partition) and the workgroup takes 256/(D/16) heads at a time. A batch of short sequences
+// then needs one small workgroup per sequence (a workgroup per row would mostly be dispatched
+// to find nothing to do). Partitions are folded in ascending order with a running (max, sum,
+// accumulator), rescaled as the max grows; the result is deterministic.
 template <int D>
-__global__ __launch_bounds__(256) void paged_decode_reduce_rows_kernel(DecodeArgs a) {
-  constexpr int LPR = D / 4;          // lanes per row
-  constexpr int S = 64 / LPR;         // partition slices of the wave
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.num_seqs * a.num_q_heads) return;
-  const int b = row / a.num_q_heads;
-  const int h = row - b * a.num_q_heads;
+__global__ __launch_bounds__(256) void paged_decode_reduce_seq_kernel(DecodeArgs a) {
+  constexpr int LPH = D / 16;         // lanes per head row
+  constexpr int HPP = 256 / LPH;      // heads per pass of the workgroup
+  const int b = blockIdx.x;
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
   if (nparts <= 1) return;
-  const int lane = threadIdx.x & 63;
-  const int sl = lane / LPR;
-  const int c = lane % LPR;
-  const size_t base = ((size_t)b * a.num_q_heads + h) * a.pmax;
-  const float* __restrict__ ml = a.ws_ml + base * 2;
-  const float4* __restrict__ acc = reinterpret_cast<const float4*>(a.ws_acc + base * D) + c;
-
-  float m = -INFINITY, den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int p = sl; p < nparts; p += S) {
-    const float mp = ml[2 * p];
-    const float lp = ml[2 * p + 1];
-    const float4 x = acc[(size_t)p * LPR];
-    const float mn = fmaxf(m, mp);
-    const float fo = m == -INFINITY ? 0.f : exp2f(m - mn);
-    const float fp = mp == -INFINITY ? 0.f : exp2f(mp - mn);
-    den = den * fo + lp * fp;
-    num.x = __builtin_fmaf(x.x, fp, num.x * fo);
-    num.y = __builtin_fmaf(x.y, fp, num.y * fo);
-    num.z = __builtin_fmaf(x.z, fp, num.z * fo);
-    num.w = __builtin_fmaf(x.w, fp, num.w * fo);
-    m = mn;
-  }
+  const int c = threadIdx.x % LPH;
+  for (int h = threadIdx.x / LPH; h < a.num_q_heads; h += HPP) {
+    const size_t base = ((size_t)b * a.num_q_heads + h) * a.pmax;
+    const float* __restrict__ ml = a.ws_ml + base * 2;
+    const float4* __restrict__ acc = reinterpret_cast<const float4*>(a.ws_acc + base * D) + c * 4;
+    float m = -INFINITY, den = 0.f;
+    float4 num[4];
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(m, off, 64);
-    const float dn = __shfl_xor(den, off, 64);
-    const float4 no = make_float4(__shfl_xor(num.x, off, 64), __shfl_xor(num.y, off, 64),
-                                  __shfl_xor(num.z, off, 64), __shfl_xor(num.w, off, 64));
-    const float M = fmaxf(m, mo);
-    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
-    const float fo = mo == -INFINITY ? 0.f : exp2f(mo - M);
-    den = __builtin_fmaf(f, den, fo * dn);
-    num.x = __builtin_fmaf(f, num.x, fo * no.x);
-    num.y = __builtin_fmaf(f, num.y, fo * no.y);
-    num.z = __builtin_fmaf(f, num.z, fo * no.z);
-    num.w = __builtin_fmaf(f, num.w, fo * no.w);
-    m = M;
+    for (int i = 0; i < 4; ++i) num[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+    for (int p = 0; p < nparts; ++p) {
+      const float mp = ml[2 * p];
+      const float lp = ml[2 * p + 1];
+      float4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = acc[(size_t)p * (D / 4) + i];
+      const float mn = fmaxf(m, mp);
+      const float fo = m == -INFINITY ? 0.f : exp2f(m - mn);   // rescale of what came before
+      const float fp = mp == -INFINITY ? 0.f : exp2f(mp - mn);  // weight of this partition
+      den = den * fo + lp * fp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        num[i].x = __builtin_fmaf(x[i].x, fp, num[i].x * fo);
+        num[i].y = __builtin_fmaf(x[i].y, fp, num[i].y * fo);
+        num[i].z = __builtin_fmaf(x[i].z, fp, num[i].z * fo);
+        num[i].w = __builtin_fmaf(x[i].w, fp, num[i].w * fo);
+      }
+      m = mn;
+    }
+    const bool ok = den > 0.f;
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[4 * i + 0] = ok ? num[i].x / den : 0.f;
+      y[4 * i + 1] = ok ? num[i].y / den : 0.f;
+      y[4 * i + 2] = ok ? num[i].z / den : 0.f;
+      y[4 * i + 3] = ok ? num[i].w / den : 0.f;
+    }
+    const size_t o = ((size_t)b * a.num_q_heads + h) * D + c * 16;
+    if (a.out_dtype == F32) {
+      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+    } else {
+      u32x4 w[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = a.out_dtype == BF16 ? narrow_bits<BF16>(y[2 * i]) : narrow_bits<F16>(y[2 * i]);
+        const uint32_t hi =
+            a.out_dtype == BF16 ? narrow_bits<BF16>(y[2 * i + 1]) : narrow_bits<F16>(y[2 * i + 1]);
+        w[i >> 2][i & 3] = lo | (hi << 16);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + o);
+      dst[0] = w[0];
+      dst[1] = w[1];
+    }
   }
-  if (sl != 0) return;
-  const size_t o = ((size_t)b * a.num_q_heads + h) * D + c * 4;
-  const bool ok = den > 0.f;
-  store_out(a.out, o + 0, ok ? num.x / den : 0.f, a.out_dtype);
-  store_out(a.out, o + 1, ok ? num.y / den : 0.f, a.out_dtype);
-  store_out(a.out, o + 2, ok ? num.z / den : 0.f, a.out_dtype);
-  store_out(a.out, o + 3, ok ? num.w / den : 0.f, a.out_dtype);
 }
 
-// Partitions per sequence up to which the one-wave merge is used.
-constexpr int kRowsReduceMaxParts = 16;
+// Partitions per sequence up to which the per-sequence merge is used.
+constexpr int kSeqReduceMaxParts = 16;
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-  if (a.pmax <= kRowsReduceMaxParts) {
-    const dim3 grid((unsigned)(((int64_t)a.num_seqs * a.num_q_heads + 3) / 4));
+  if (a.pmax <= kSeqReduceMaxParts) {
+    const dim3 grid((unsigned)a.num_seqs);
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<64>, grid, dim3(256), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<128>, grid, dim3(256), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(paged_decode_reduce_rows_kernel<256>, grid, dim3(256), 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(paged_decode_reduce_seq_kernel<64>, grid, dim3(256), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(paged_decode_reduce_seq_kernel<128>, grid, dim3(256), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(paged_decode_reduce_seq_kernel<256>, grid, dim3(256), 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

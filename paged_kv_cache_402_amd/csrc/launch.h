@@ -42,7 +42,28 @@ struct DecodeArgs {
   // of (-1: none). The pass copies it (this KV head's tile, all rows but the new token's)
   // into the sequence's last block and reads the earlier tokens from it (null: no copies).
   const int32_t* cow_src;
+  // Measurement only (null: off): workgroup w < timeline_cap of the per-partition pass writes
+  // {start, end, HW_ID, XCC_ID} at 4 w (clock: s_memrealtime, 100 MHz).
+  uint32_t* timeline;
+  int timeline_cap;
+  // Scheduling word of a work-list launch (the workspace's first 8 bytes; null: static
+  // assignment only): {high 32 bits kSchedCookie once initialised, low 32 bits tickets taken}.
+  // Workgroups w >= sched_static of the launch take work unit sched_static + ticket instead
+  // of unit w, in the list's order, so units go to workgroups in the order they start; the
+  // holder of the last ticket sets the count back to 0. The launch code sets sched_static to
+  // the number of workgroups resident at once.
+  unsigned long long* sched;
+  int sched_static;
 };
+
+// Bytes of the workspace header that holds the scheduling word.
+constexpr size_t kWsHeaderBytes = 256;
+constexpr unsigned kSchedCookie = 0x5CED0DE1u;
+// Writes the initialised scheduling word {kSchedCookie, 0} (a one-lane kernel).
+hipError_t launch_sched_init(unsigned long long* sched, hipStream_t stream);
+
+// Process-wide timeline buffer picked up by every later per-partition launch (measurement).
+void decode_timeline(uint32_t** buf, int* cap);
 
 // Bytes of dynamic LDS one decode workgroup needs.
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part);

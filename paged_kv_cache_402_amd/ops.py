@@ -47,6 +47,16 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: 
                                               block_size, head_dim, partition_size))
 
 
+def decode_workspace_init(workspace):
+    """Initialises the workspace's scheduling word (pkv_decode_workspace_init): work-list
+    launches then hand the units of late-starting workgroups out in list order."""
+    _dev(workspace, "workspace")
+    check(lib.pkv_decode_workspace_init(workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(workspace)), "decode_workspace_init")
+    return workspace
+
+
 def default_partition(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                       block_size: int, max_blocks_per_seq: int) -> int:
     """The partition size pkv_decode_default_partition picks for these shapes (a multiple of
@@ -166,7 +176,7 @@ def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
     if workspace is None:
         if need == 0:
             return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace_init(torch.empty(need, dtype=torch.uint8, device=q.device))
     _dev(workspace, "workspace")
     return workspace, workspace.numel() * workspace.element_size()
 

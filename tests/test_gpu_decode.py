@@ -997,3 +997,103 @@ def test_append_decode_skips_an_invalid_last_block():
     changed = (kd.view(torch.int16) != before.view(torch.int16)).any(dim=(1, 2, 3))
     # only sequence 0's last block took a store
     assert changed.nonzero().flatten().tolist() == [int(case.block_tables[0, 2])]
+
+
+# --------------------------------------------------------------------------------------------
+# work-list launches with an initialised workspace: late workgroups take their units in list
+# order from the workspace's scheduling word
+# --------------------------------------------------------------------------------------------
+
+def _sched_word(ws):
+    return int(ws[:8].cpu().numpy().view(np.uint64)[0])
+
+
+@pytest.mark.parametrize("shape", ["gqa_short", "mha_mixed", "packed", "append_step"])
+def test_scheduled_units_are_each_taken_once_and_bitwise_static(shape):
+    """Units handed out by the scheduling word: every (row, KV head) unit of the list is taken
+    by exactly one workgroup (read from the per-workgroup timeline, which records the unit),
+    some workgroups took a unit other than their own index (the dynamic path ran), the output
+    is bitwise that of the same launch over a workspace that was never initialised (static
+    units), three calls in a row give the same bits, and each call leaves the word initialised
+    with its count back at 0."""
+    import paged_kv_cache_402_amd as pk
+    from paged_kv_cache_402_amd._lib import lib as plib
+    rng = np.random.default_rng(7300)
+    if shape == "gqa_short":
+        lens = [int(x) for x in rng.integers(1, 700, size=700)]
+        case = gen.make_case("sch1", rng, lens, 32, 8, 128, 16, "bf16", values=False)
+        part, pack = 256, 0
+    elif shape == "mha_mixed":
+        lens = [int(x) for x in rng.integers(1, 1500, size=90)]
+        case = gen.make_case("sch2", rng, lens, 40, 40, 128, 32, "f16", values=False)
+        part, pack = 512, 0
+    elif shape == "packed":
+        lens = [int(x) for x in rng.integers(1, 300, size=900)]
+        case = gen.make_case("sch3", rng, lens, 16, 8, 128, 16, "bf16", values=False)
+        part, pack = 256, 32
+    else:
+        lens = [int(x) for x in rng.integers(2, 900, size=400)]
+        case = gen.make_case("sch4", rng, lens, 32, 8, 64, 16, "bf16", values=False)
+        part, pack = 256, 0
+    dt = case.dtype
+    B, Hq, D, Hkv = len(lens), case.num_q_heads, case.head_dim, case.num_kv_heads
+    W, bs = case.block_tables.shape[1], case.block_size
+    shape4 = (case.num_blocks, Hkv, bs, D)
+    k = gen.device_normal(shape4, dt, 7301, "cuda")
+    v = gen.device_normal(shape4, dt, 7302, "cuda")
+    q = gen.device_normal((B, Hq, D), dt, 7303, "cuda")
+    tables, lns = i32(case.block_tables), i32(case.seq_lens)
+    if pack:
+        items, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, part, pack)
+    else:
+        items = pk.decode_work_list(case.seq_lens, W, bs, part)
+        rows = items.shape[0]
+    work = i32(items)
+    units = rows * Hkv
+    need = pk.decode_workspace_bytes(B, Hq, W, bs, D, part)
+    assert need > 0
+
+    def run(ws, timeline=None):
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        if timeline is not None:
+            pk.check(plib.pkv_debug_timeline(timeline.data_ptr(), units), "debug_timeline")
+        try:
+            if shape == "append_step":
+                k_new = gen.device_normal((B, Hkv, D), dt, 7304, "cuda")
+                v_new = gen.device_normal((B, Hkv, D), dt, 7305, "cuda")
+                kk, vv = k.clone(), v.clone()
+                pk.paged_attention_decode_append(out, q, k_new, v_new, kk, vv, tables, lns,
+                                                 case.scale, partition_size=part, workspace=ws,
+                                                 work_list=(work, rows) if pack else work)
+            else:
+                pk.paged_attention_decode(out, q, k, v, tables, lns, case.scale,
+                                          partition_size=part, workspace=ws,
+                                          work_list=(work, rows) if pack else work)
+            torch.cuda.synchronize()
+        finally:
+            pk.check(plib.pkv_debug_timeline(None, 0), "debug_timeline")
+        return out
+
+    ws_static = torch.zeros(need, dtype=torch.uint8, device="cuda")     # never initialised
+    want = run(ws_static)
+    # each late workgroup's add found no cookie and kept its static unit: the count grew, the
+    # high half stayed without the cookie
+    assert _sched_word(ws_static) >> 32 == 0 and _sched_word(ws_static) > 0
+    ws = pk.decode_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    cookie = _sched_word(ws)
+    assert cookie >> 32 != 0 and cookie & 0xFFFFFFFF == 0
+    tl = torch.zeros(8 * units, dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        tl.zero_()
+        got = run(ws, tl)
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), rep
+        assert _sched_word(ws) == cookie, rep
+        rec = tl.cpu().numpy().view(np.uint32).reshape(-1, 8)
+        # every workgroup of these lists has work (and the first lane of a packed row holds a
+        # real item), so every one recorded its unit: each unit exactly once
+        assert (rec[:, 1] != 0).all(), rep
+        taken = np.sort(rec[:, 4])
+        assert np.array_equal(taken, np.arange(units)), rep
+        assert (rec[:, 4] != np.arange(units)).any()        # the scheduling word was used
+    assert np.isfinite(want.cpu().numpy()).all()
