@@ -479,6 +479,19 @@ def timeline_summary(tl, items, num_kv_heads, part, lens, kv_row_bytes):
     xcc = rec[ok, 3] & 0xF
     first_k = float(np.sort(start)[min(len(start) - 1, peak - 1)])
     head = unit % num_kv_heads
+    # phases of wave 0 (start -> end of K pass -> end of V pass -> end), by partition length
+    tk = (rec[ok, 5] - rec[ok, 0]) / 100.0
+    tv = (rec[ok, 6] - rec[ok, 5]) / 100.0
+    te = (rec[ok, 1] - rec[ok, 6]) / 100.0
+    phases = {}
+    for lo, hi in ((0, 32), (32, 128), (128, 512), (512, 1024), (1024, 4096)):
+        sel = (n >= lo) & (n < hi) & (rec[ok, 5] != 0) & (rec[ok, 6] != 0)
+        if sel.any():
+            phases["%d-%d" % (lo, hi - 1)] = {
+                "workgroups": int(sel.sum()),
+                "to_k_end_us": round(float(np.median(tk[sel])), 2),
+                "k_end_to_v_end_us": round(float(np.median(tv[sel])), 2),
+                "v_end_to_end_us": round(float(np.median(te[sel])), 2)}
     # bandwidth estimate: each workgroup's KV bytes (K and V rows of its tokens, one head)
     # spread evenly over its lifetime, summed per 5 us window
     kv_bytes = 2 * n.astype(np.float64) * kv_row_bytes
@@ -506,6 +519,7 @@ def timeline_summary(tl, items, num_kv_heads, part, lens, kv_row_bytes):
             "mean_duration_us": round(float(dur.mean()), 2),
             "last_end_per_xcd_us": [round(float(end[xcc == x].max()), 2) if (xcc == x).any()
                                     else None for x in range(8)],
+            "phases_median_by_tokens": phases,
             "kv_TBps_mean": round(mean_bw, 3),
             "kv_TBps_per_5us": [round(float(x), 2) for x in bw_tbps]}
 
@@ -907,6 +921,7 @@ def main():
         "ms_per_step_median": round(float(np.median(step_ms)), 5),
         "ms_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)), 5),
                                 round(float(np.percentile(step_ms, 90)), 5)],
+        "ms_each_step": [round(float(x), 4) for x in step_ms],
         "timing": "wall clock over back-to-back steps (warm caches)" if args.warm else
                   ("HIP events around each step's launches (none between them), 1 GiB read "
                    "before each (cold L2 and memory-side cache); wall clock incl. the eviction "

@@ -385,8 +385,8 @@ int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int3
  * point) writes, for each of its workgroups w < capacity, eight uint32 at buf + 8 w: start
  * and end time (s_memrealtime, a 100 MHz clock, low 32 bits), the HW_ID register (CU, SIMD
  * and shader-engine ids), the XCC_ID register (XCD), the work unit it took (work-list
- * launches: row * num_kv_heads + KV head; else w) and three zeros, from the workgroup's first
- * lane. Workgroups that find no work (list entries past a sequence's end) write nothing, so
+ * launches: row * num_kv_heads + KV head; else w), the times its first wave finished its key
+ * pass and its value pass, and the tokens of its partition, from the workgroup's first lane. Workgroups that find no work (list entries past a sequence's end) write nothing, so
  * clear the buffer first. buf: device, 16-byte aligned, 32 * capacity bytes, owned by the
  * caller and kept alive until the timeline is switched off with capacity 0. Process-wide;
  * not for concurrent use with launches on other threads. */

@@ -151,16 +151,22 @@ hipError_t launch_sched_init(unsigned long long* sched, hipStream_t stream) {
 }
 
 // Measurement only: workgroup start and end (s_memrealtime, 100 MHz) and where it ran.
+// t_k / t_v: when wave 0 finished its K pass / its V pass (0 where it has none).
 __device__ __forceinline__ void record_timeline(const DecodeArgs& a, uint32_t t_start,
-                                                unsigned unit) {
+                                                unsigned unit, uint32_t t_k, uint32_t t_v,
+                                                uint32_t tokens) {
   if (a.timeline != nullptr && threadIdx.x == 0 && blockIdx.x < (unsigned)a.timeline_cap) {
     const uint32_t t_end = (uint32_t)__builtin_amdgcn_s_memrealtime();
     const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_REG_HW_ID
     const uint32_t xcc_id = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // HW_REG_XCC_ID
     uint32_t* rec = a.timeline + 8 * (size_t)blockIdx.x;
     store16(rec, u32x4{t_start, t_end, hw_id, xcc_id});
-    store16(rec + 4, u32x4{unit, 0u, 0u, 0u});
+    store16(rec + 4, u32x4{unit, t_k, t_v, tokens});
   }
+}
+
+__device__ __forceinline__ uint32_t timeline_now(const DecodeArgs& a) {
+  return a.timeline != nullptr ? (uint32_t)__builtin_amdgcn_s_memrealtime() : 0u;
 }
 
 template <int DT, int D, int G, bool MF>
@@ -206,12 +212,34 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     pi = blockIdx.y;
     b = blockIdx.z;
   }
+  const int t0 = pi * a.part;                  // a multiple of the block size
+  // ---- block ids of the partition (one per lane) and the query slices, issued together with
+  // the length load: every table entry the partition could use (those past the sequence end
+  // are never read again), so no load waits on another before the first K round ----
+  const int32_t* __restrict__ trow =
+      a.block_tables + (size_t)b * a.max_blocks + (t0 >> a.bs_log2);
+  const int pblk = min(a.part >> a.bs_log2, a.max_blocks - (t0 >> a.bs_log2));
+  int ids[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = k * 64 + lane;
+    ids[k] = j < pblk ? trow[j] : 0;
+  }
+  const int kr = lane / K::LK;  // token row inside a K step
+  const int kc = lane % K::LK;  // this lane's vectors: kc, kc+LK, ...
+  const unsigned char* qsrc =
+      (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * K::RB;
+  u32x4 qv[G][K::NLK];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < K::NLK; ++i)
+      qv[g][i] = load16(qsrc + (size_t)(g * K::C + kc + i * K::LK) * 16);
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
   if (pi >= nparts) return;
-  const int t0 = pi * a.part;                  // a multiple of the block size
   const int n = max(0, min(L - t0, a.part));   // tokens of this partition
   // a packed wave's partition must fit its LDS area (the list builder packs at most
   // part / 4 tokens); a list that breaks this leaves the item unwritten
@@ -241,16 +269,6 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const unsigned char* kbase = (const unsigned char*)a.k_cache + kvh * head_bytes;
   const unsigned char* vbase = (const unsigned char*)a.v_cache + kvh * head_bytes;
 
-  // ---- block ids of the partition (one per lane) and the query slices ----
-  const int nblk = (n + bs_mask) >> a.bs_log2;
-  const int32_t* __restrict__ trow =
-      a.block_tables + (size_t)b * a.max_blocks + (t0 >> a.bs_log2);
-  int ids[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int j = k * 64 + lane;
-    ids[k] = j < nblk ? trow[j] : 0;
-  }
   // ---- appended token (optional): the K and V rows of token L - 1 come from k_new /
   // v_new instead of the cache, and the workgroup of (KV head, last partition) stores them
   // into the cache slot the table gives; no other workgroup reads that slot in this launch
@@ -322,16 +340,6 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       if (k == (jb >> 6) && lane == (jb & 63)) ids[k] = cow;
   }
 
-  const int kr = lane / K::LK;  // token row inside a K step
-  const int kc = lane % K::LK;  // this lane's vectors: kc, kc+LK, ...
-  const unsigned char* qsrc =
-      (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * K::RB;
-  u32x4 qv[G][K::NLK];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < K::NLK; ++i)
-      qv[g][i] = load16(qsrc + (size_t)(g * K::C + kc + i * K::LK) * 16);
 
   // ---- K pass over the wave's share: scores (log2 units) -> LDS, running max ----
   float m[G];
@@ -451,6 +459,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   for (int g = 0; g < G; ++g) m[g] = xor_max_from<K::LK>(m[g]);
   }
 
+  const uint32_t t_k = timeline_now(a);
+
   // ---- first round of V loads, issued before the exponentials ----
   const int vr = lane / K::LV;
   const int vc = lane % K::LV;
@@ -528,6 +538,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
   }
 
+  const uint32_t t_v = timeline_now(a);
+
   // ---- the wave's rows summed; the wave's (max, sum, accumulator) -> LDS ----
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       }
     }
     cow_copy();
-    record_timeline(a, t_start, unit);
+    record_timeline(a, t_start, unit, t_k, t_v, (uint32_t)n);
     return;
   }
   // every lane's score reads are done before the area is reused (LDS keeps a wave's order)
@@ -615,7 +627,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
   }
   cow_copy();
-  record_timeline(a, t_start, unit);
+  record_timeline(a, t_start, unit, t_k, t_v, (uint32_t)n);
 }
 
 // Merge of the partitions of one (sequence, query head):
@@ -731,10 +743,13 @@ static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
   const auto kernel = paged_decode_partition_kernel<DT, D, G, MF>;
   if (a.work != nullptr) {
     const int units = a.num_kv_heads * a.work_items;
-    // the first resident round keeps its static units; dynamic units only pay off after it
+    // Only the last machine-full of units (as many as fit at once) is handed out by ticket:
+    // the list runs longest first, so those are its shortest units, enough to even out the
+    // XCDs' finishing times, while every earlier workgroup keeps its static unit and skips the
+    // ticket's round trip (which a short, latency-bound unit feels).
     const int resident = a.sched != nullptr ? resident_groups((const void*)kernel, lds) : 0;
     if (resident <= 0 || resident >= units) a.sched = nullptr;
-    a.sched_static = resident;
+    a.sched_static = units - resident > resident ? units - resident : resident;
     hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kDecodeThreads), lds, stream, a);
   } else {
     a.sched = nullptr;
