@@ -40,6 +40,12 @@ BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk
                    "tiny")
 
 
+# Packed work lists pay off on batches of short, latency-bound partitions (measured on one
+# MI355X, cold steps): the long-tail mix 57.4 -> 53.1 us at 256 tokens (512: 62.9 us); the
+# short batch 124.7 -> 82.8 us at 48.
+DEFAULT_PACK = {"llama13b_longtail": 256, "llama3_8b_short_batch": 48}
+
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -56,9 +62,10 @@ def parse_args():
     p.add_argument("--append", choices=("fused", "separate"), default="fused",
                    help="fused: the decode pass stores the new tokens' K/V itself; separate: "
                         "reshape_and_cache runs first as its own launch")
-    p.add_argument("--pack", type=int, default=0,
+    p.add_argument("--pack", type=int, default=-1,
                    help="with --grid list: partitions of at most this many tokens run four to a "
-                        "workgroup, one wave each (0: none)")
+                        "workgroup, one wave each (0: none; -1: the workload's measured best, "
+                        "%s, else 0)" % ", ".join("%s %d" % kv for kv in DEFAULT_PACK.items()))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -72,6 +79,9 @@ def parse_args():
                    help="after the timed steps, run 3 more with the per-workgroup timeline of the "
                         "decode partition kernel switched on (pkv_debug_timeline) and report "
                         "ramp-up, occupancy, tail and per-workgroup fixed cost")
+    p.add_argument("--no-sched", action="store_true",
+                   help="leave the workspace's scheduling word uninitialised: every workgroup of "
+                        "a work-list launch keeps its static unit (for comparison)")
     p.add_argument("--no-read-probe", action="store_true",
                    help="leave the short read probe (achievable_GBps) out of the headline run")
     p.add_argument("--warm", action="store_true",
@@ -141,6 +151,7 @@ def build_state(name, pk, gen, torch, dev):
             "pairs": torch.from_numpy(np.ascontiguousarray(pairs.reshape(-1, 2))).to(dev)
             if pairs.shape[0] else None,
             "cow_src": torch.from_numpy(cow_src).to(dev),
+            "cow_src_host": cow_src, "slots_host": slots,
             "out": torch.empty((B, case.num_q_heads, case.head_dim), dtype=tdt, device=dev),
         }
     maker = gen.WORKLOADS[name]
@@ -750,6 +761,8 @@ def main():
         serve_report(pk, torch, dev, args.serve_steps)
         return
 
+    if args.pack < 0:
+        args.pack = DEFAULT_PACK.get(args.workload, 0)
     log("setting up %s" % args.workload)
     st = build_state(args.workload, pk, gen, torch, dev)
     case = st["case"]
@@ -792,8 +805,10 @@ def main():
     ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
                                          case.block_size, case.head_dim, part)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
-    if ws_bytes:
+    if ws_bytes and not args.no_sched:
         pk.decode_workspace_init(ws)     # list launches hand out late units from its header
+    elif ws_bytes:
+        ws.zero_()                       # no scheduling cookie: static units only
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
@@ -813,6 +828,13 @@ def main():
         eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
         row = case.num_kv_heads * case.head_dim * eb
         bytes_["decode_kernel"] += int(st["pairs"].shape[0]) * 2 * (case.block_size - 1) * row
+        # a copying sequence reads its last block's earlier rows from the source block (which
+        # its siblings list too), not from the copy: those rows of the copy are written, never
+        # read, so they leave the distinct bytes read
+        copied = st["cow_src_host"] >= 0
+        skipped = int((st["slots_host"][copied] % case.block_size).sum())
+        bytes_["kv_unique"] -= skipped * case.kv_bytes_per_token()
+        bytes_["decode_kernel"] -= skipped * case.kv_bytes_per_token()
     stages = (["copy_blocks"] if st["pairs"] is not None and not fused_cow else []) + \
         ([] if fused else ["reshape_and_cache"]) + \
         (["shared_prefix"] if members is not None and pp > 0 else []) + \
@@ -937,7 +959,7 @@ def main():
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "kv_dtype": case.dtype, "accumulate": "f32", "partition_size": part,
-                   "grid": args.grid,
+                   "grid": args.grid, "late_units": "static" if args.no_sched else "ticketed",
                    "pack_tokens": args.pack if args.grid == "list" else 0,
                    "append": "fused" if fused else "separate",
                    "copy_on_write": ("fused" if fused_cow else "separate")
