@@ -82,6 +82,9 @@ def parse_args():
     p.add_argument("--no-sched", action="store_true",
                    help="leave the workspace's scheduling word uninitialised: every workgroup of "
                         "a work-list launch keeps its static unit (for comparison)")
+    p.add_argument("--kv-policy", choices=("auto", "stream", "cached"), default="auto",
+                   help="cache policy of the decode kernel's KV reads; auto: "
+                        "pkv_decode_kv_policy on the workload's tables")
     p.add_argument("--no-read-probe", action="store_true",
                    help="leave the short read probe (achievable_GBps) out of the headline run")
     p.add_argument("--warm", action="store_true",
@@ -428,10 +431,15 @@ def probe_patterns(full):
     return pats
 
 
+PROBE_POLICIES = (("default", False), ("nontemporal", True))
+
+
 def read_probe(pk, torch, dev, full, reps=10):
-    """Plain-read bandwidth of each pattern: 2 warm-up launches, then `reps` launches, each
-    after a 1 GiB read of other data (cold L2 and memory-side cache, as the decode timing);
-    HIP events on the launch stream around each; GB/s = bytes read / median launch time."""
+    """Plain-read bandwidth of each pattern under each load cache policy (the default one, and
+    the non-temporal one of the attention kernels' KV-row loads): 2 warm-up launches, then
+    `reps` launches, each after a 1 GiB read of other data (cold L2 and memory-side cache, as
+    the decode timing); HIP events on the launch stream around each; GB/s = bytes read /
+    median launch time."""
     buf = torch.ones(PROBE_POOL_BYTES // 4, dtype=torch.float32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -439,28 +447,38 @@ def read_probe(pk, torch, dev, full, reps=10):
     res = []
     for name, tb, ids, tpw, what in probe_patterns(full):
         d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
-        for _ in range(2):
-            pk.read_probe(buf, tb, d_ids, tpw, sink)
-        ts = []
-        for _ in range(reps):
-            torch.sum(evict, dim=0, out=evict_sum)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            pk.read_probe(buf, tb, d_ids, tpw, sink)
-            e1.record()
-            ts.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ts])
-        nbytes = int(len(ids)) * tb
-        res.append({"pattern": name, "bytes": nbytes, "tile_bytes": tb,
-                    "workgroups": -(-len(ids) // tpw), "median_ms": round(float(np.median(ms)), 5),
-                    "GBps": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
-                    "GBps_p10_p90": [round(nbytes / (float(np.percentile(ms, q)) * 1e-3) / 1e9, 1)
-                                     for q in (90, 10)],
-                    "what": what})
-        log("read probe %s: %.1f GB/s" % (name, res[-1]["GBps"]))
+        for policy, nt in PROBE_POLICIES:
+            for _ in range(2):
+                pk.read_probe(buf, tb, d_ids, tpw, sink, nontemporal=nt)
+            ts = []
+            for _ in range(reps):
+                torch.sum(evict, dim=0, out=evict_sum)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                pk.read_probe(buf, tb, d_ids, tpw, sink, nontemporal=nt)
+                e1.record()
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in ts])
+            nbytes = int(len(ids)) * tb
+            res.append({"pattern": name, "policy": policy, "bytes": nbytes, "tile_bytes": tb,
+                        "workgroups": -(-len(ids) // tpw),
+                        "median_ms": round(float(np.median(ms)), 5),
+                        "GBps": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
+                        "GBps_p10_p90": [round(nbytes / (float(np.percentile(ms, q)) * 1e-3)
+                                               / 1e9, 1) for q in (90, 10)],
+                        "what": what})
+            log("read probe %s, %s policy: %.1f GB/s" % (name, policy, res[-1]["GBps"]))
     del buf, evict
     return res
+
+
+def probe_rate(probe, pattern, policy):
+    for r in probe:
+        if r["pattern"] == pattern and r["policy"] == policy:
+            return r["GBps"]
+    raise KeyError((pattern, policy))
 
 
 def timeline_summary(tl, items, num_kv_heads, part, lens, kv_row_bytes):
@@ -599,7 +617,8 @@ def serve_loop(pk, torch, dev, steps, static=False, warm_steps=None):
             d_work[:items.shape[0]].copy_(h_work[:items.shape[0]], non_blocking=True)
             pk.paged_attention_decode(out[:n], q[:n], k, v, d_tab[:n * W].view(n, W), d_lens[:n],
                                       0.0884, partition_size=part, workspace=ws,
-                                      work_list=d_work[:items.shape[0]])
+                                      work_list=d_work[:items.shape[0]],
+                                      kv_policy=pk.decode_kv_policy(tab, lens, bs, NB))
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         if step >= warm_steps:
@@ -770,7 +789,7 @@ def main():
                                                   case.num_kv_heads, case.head_dim,
                                                   case.block_size, case.table_width)
     bytes_ = byte_model(case, part)
-    work, members, pp = None, None, 0
+    work, members, pp, items = None, None, 0, None
     if args.grid == "list" and args.pack > 0:
         items, rows = pk.decode_work_list_packed(case.seq_lens, case.table_width,
                                                  case.block_size, part, args.pack)
@@ -801,6 +820,14 @@ def main():
         bytes_["decode_kernel"] += 4 * int(items.shape[0]) - sb["kv"] - sb["tables"] - sb["partials"]
         bytes_["prefix_kernel"] = sb["prefix_kernel"]
         log("shared prefix: %d members, %d partitions" % (mem.shape[0], pp))
+    # cache policy of the per-partition pass's KV reads, from the tables and the partitions
+    # that pass reads (pkv_decode_kv_policy; the shared-prefix list leaves the shared
+    # partitions to the prefix pass)
+    policy = {"stream": pk.KV_STREAM, "cached": pk.KV_CACHED}.get(args.kv_policy)
+    if policy is None:
+        policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, case.block_size,
+                                     case.num_blocks, work_list=items, partition_size=part)
+    log("KV read policy: %s" % ("cached" if policy == pk.KV_CACHED else "stream"))
     # no workspace: no sequence spans two partitions and the merge pass has nothing to do
     ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
                                          case.block_size, case.head_dim, part)
@@ -852,17 +879,17 @@ def main():
             pk.paged_attention_partitions_step(st["out"], st["q"], st["k_new"], st["v_new"],
                                                st["cow_src"], st["k"], st["v"], st["tables"],
                                                st["lens"], case.scale, partition_size=part,
-                                               workspace=ws, work_list=work)
+                                               workspace=ws, work_list=work, kv_policy=policy)
         elif name == "decode_partitions" and fused:
             pk.paged_attention_partitions_append(st["out"], st["q"], st["k_new"], st["v_new"],
                                                  st["k"], st["v"], st["tables"], st["lens"],
                                                  case.scale, partition_size=part, workspace=ws,
-                                                 work_list=work)
+                                                 work_list=work, kv_policy=policy)
         elif name == "decode_partitions":
             # paged_attention_decode's two launches, called apart so each has its own events
             pk.paged_attention_partitions(st["out"], st["q"], st["k"], st["v"], st["tables"],
                                           st["lens"], case.scale, partition_size=part,
-                                          workspace=ws, work_list=work)
+                                          workspace=ws, work_list=work, kv_policy=policy)
         else:
             pk.paged_attention_reduce(st["out"], st["lens"], case.block_size, case.table_width,
                                       ws, partition_size=part)
@@ -960,6 +987,7 @@ def main():
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "kv_dtype": case.dtype, "accumulate": "f32", "partition_size": part,
                    "grid": args.grid, "late_units": "static" if args.no_sched else "ticketed",
+                   "kv_policy": "cached" if policy == pk.KV_CACHED else "stream",
                    "pack_tokens": args.pack if args.grid == "list" else 0,
                    "append": "fused" if fused else "separate",
                    "copy_on_write": ("fused" if fused_cow else "separate")
@@ -989,11 +1017,14 @@ def main():
     if not args.no_read_probe:
         log("read probe (achievable read bandwidth)")
         probe = read_probe(pk, torch, dev, full=False)
-        ach = probe[0]["GBps"]
+        ach = probe_rate(probe, "stream_2GiB", "nontemporal")
         result["achievable_GBps"] = ach
-        result["achievable_note"] = ("plain 2 GiB streaming read measured on this device "
-                                     "(pkv_read_probe), beside the nominal %.0f GB/s peak"
-                                     % HBM_PEAK_GBPS)
+        result["achievable_note"] = ("2 GiB streaming read with the KV loads' non-temporal "
+                                     "cache policy, measured on this device (pkv_read_probe; "
+                                     "%.1f GB/s with the default policy), beside the nominal "
+                                     "%.0f GB/s peak"
+                                     % (probe_rate(probe, "stream_2GiB", "default"),
+                                        HBM_PEAK_GBPS))
         result["frac_of_achievable"] = round(gbps / ach, 4)
         result["read_probe"] = probe
     if args.timeline:

@@ -90,14 +90,38 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int max_blocks_
 
 /* Initialises a workspace's scheduling word (one tiny kernel on stream; no allocation, no
  * memset). Optional: the per-partition pass over a work list (the _list, _append, _step and
- * _shared entry points) then hands the work units of the workgroups that start after the
- * first resident round out in the list's order from that word, one atomic per workgroup, so
+ * _shared entry points) then hands the work units of its last workgroups (half as many as
+ * are resident at once) out in the list's order from that word, one atomic per workgroup, so
  * the last, short partitions go to whichever XCD has room instead of a fixed eighth of them to
  * each; the output is bitwise the same either way. Each call leaves the word initialised, so
  * once per workspace (for instance right after allocating it) is enough. A workspace that was
  * never initialised works too, with the fixed assignment. Calls sharing a workspace must not
  * overlap in time (already required by the partials). A workspace_bytes of 0 is a no-op. */
 int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cache policy of a decode launch's KV reads (a gfx950 matter; no page defines it). Every KV
+ * row of a sequence is read once per launch, so by default the reads are non-temporal
+ * (PKV_KV_STREAM: global_load ... nt), which reads HBM about 12% faster. Blocks that several
+ * sequences of the batch list (P1 §6.1-6.2; P3 §2.2.8: forks of parallel sampling and beam
+ * search, a common prompt prefix) are read again by other workgroups of the same launch;
+ * where such repeats are most of the reads, the default policy (PKV_KV_CACHED) keeps those
+ * lines in L2 for them and is faster. */
+enum { PKV_KV_STREAM = 0, PKV_KV_CACHED = 1 };
+
+/* The policy for one launch, from host copies of its block tables ([num_seqs]
+ * [max_blocks_per_seq]) and seq_lens: PKV_KV_CACHED when at least half of the launch's block
+ * reads repeat a block another read already names, i.e. reads >= 2 x distinct blocks; else
+ * PKV_KV_STREAM. The reads are the in-pool table entries of the tokens the launch attends
+ * (lengths clamped to the table): every token of every sequence with work_list NULL, else
+ * those of the partitions (of partition_size tokens, a multiple of block_size) that the host
+ * list's list_len entries name: a list from pkv_decode_work_list, all of a packed list from
+ * pkv_decode_work_list_packed (its packed-row entries are skipped, the items they point at are
+ * counted where they stand), or the list of pkv_decode_plan_shared_prefix, which leaves the
+ * shared partitions to the shared-prefix pass. O(reads + num_blocks) on the host; negative on
+ * bad arguments. */
+int pkv_decode_kv_policy(const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                         int max_blocks_per_seq, int block_size, int num_blocks,
+                         const int32_t* work_list, int list_len, int partition_size);
 
 /* Decode attention over the paged cache (P1 §4.2; P2 §3.1; P3 §2.2.4: the kernel reads
  * KV block by block through the block table).
@@ -116,6 +140,9 @@ int pkv_decode_workspace_init(void* workspace, size_t workspace_bytes, void* str
  *                  only if workspace_bytes is 0 and no sequence can span two partitions
  *                  (max_blocks_per_seq*block_size <= partition_size). Calls that share a
  *                  workspace must not overlap in time (enqueue them on one stream).
+ *   kv_policy    : cache policy of the KV reads (PKV_KV_STREAM or PKV_KV_CACHED, else
+ *                  PKV_EINVAL); it changes speed only, never a bit of the output.
+ *                  pkv_decode_kv_policy picks it from the block tables.
  * Two launches: per-partition attention, then (when some sequence spans two partitions) a
  * deterministic merge of the partitions' partials.
  * The output is a deterministic function of the inputs: it does not depend on where the
@@ -125,7 +152,8 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                const int32_t* seq_lens, int num_seqs, int num_q_heads,
                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                int max_blocks_per_seq, float scale, int partition_size,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               void* workspace, size_t workspace_bytes,
+                               int kv_policy, void* stream);
 
 /* pkv_paged_attention_decode for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same two launches
@@ -145,7 +173,7 @@ int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q,
                                        int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_dim, int block_size, int num_blocks,
                                        int max_blocks_per_seq, float scale, int partition_size,
-                                       void* stream);
+                                       int kv_policy, void* stream);
 
 /* The two launches of pkv_paged_attention_decode, exposed separately so a caller can time or
  * schedule them apart. Same arguments and results as the combined call:
@@ -160,7 +188,7 @@ int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, cons
                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                    int block_size, int num_blocks, int max_blocks_per_seq,
                                    float scale, int partition_size, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   size_t workspace_bytes, int kv_policy, void* stream);
 int pkv_paged_attention_reduce(void* out, int out_dtype, const int32_t* seq_lens, int num_seqs,
                                int num_q_heads, int head_dim, int block_size,
                                int max_blocks_per_seq, int partition_size,
@@ -218,7 +246,7 @@ int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, con
                                     int block_size, int num_blocks, int max_blocks_per_seq,
                                     float scale, int partition_size, const int32_t* work_list,
                                     int work_items, void* workspace, size_t workspace_bytes,
-                                    void* stream);
+                                    int kv_policy, void* stream);
 int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
                                         const void* k_cache, const void* v_cache, int kv_dtype,
                                         const int32_t* block_tables, const int32_t* seq_lens,
@@ -226,7 +254,7 @@ int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
                                         int head_dim, int block_size, int num_blocks,
                                         int max_blocks_per_seq, float scale, int partition_size,
                                         const int32_t* work_list, int work_items, void* workspace,
-                                        size_t workspace_bytes, void* stream);
+                                        size_t workspace_bytes, int kv_policy, void* stream);
 
 /* Decode with the cache write of the step's new tokens fused in (P1 §4.3; P3 §2.2.3: the
  * newest token's K/V are stored into the block the table gives, then attended to): k_new and
@@ -247,7 +275,7 @@ int pkv_paged_attention_decode_append(void* out, int out_dtype, const void* q, c
                                       int num_blocks, int max_blocks_per_seq, float scale,
                                       int partition_size, const int32_t* work_list,
                                       int work_items, void* workspace, size_t workspace_bytes,
-                                      void* stream);
+                                      int kv_policy, void* stream);
 /* Its per-partition pass alone (the merge is pkv_paged_attention_reduce). */
 int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* q,
                                           const void* k_new, const void* v_new, void* k_cache,
@@ -258,7 +286,7 @@ int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* 
                                           int max_blocks_per_seq, float scale,
                                           int partition_size, const int32_t* work_list,
                                           int work_items, void* workspace,
-                                          size_t workspace_bytes, void* stream);
+                                          size_t workspace_bytes, int kv_policy, void* stream);
 
 /* One decode step in one pass (P1 §6.2, §4.3; P2 §2.2): the copy-on-write of each sequence's
  * last block, the cache write of its new token and the attention. cow_src (device int32
@@ -279,7 +307,8 @@ int pkv_paged_attention_decode_step(void* out, int out_dtype, const void* q, con
                                     int num_kv_heads, int head_dim, int block_size,
                                     int num_blocks, int max_blocks_per_seq, float scale,
                                     int partition_size, const int32_t* work_list, int work_items,
-                                    void* workspace, size_t workspace_bytes, void* stream);
+                                    void* workspace, size_t workspace_bytes,
+                                    int kv_policy, void* stream);
 /* Its per-partition pass alone (the merge is pkv_paged_attention_reduce). */
 int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
                                         const void* k_new, const void* v_new,
@@ -290,7 +319,7 @@ int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
                                         int num_blocks, int max_blocks_per_seq, float scale,
                                         int partition_size, const int32_t* work_list,
                                         int work_items, void* workspace, size_t workspace_bytes,
-                                        void* stream);
+                                        int kv_policy, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Shared-prefix decode (P1 §6.1; P3 §2.2.3, §2.2.8: sequences that start with the same
@@ -340,7 +369,7 @@ int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
                                       const int32_t* members, int num_members,
                                       int prefix_partitions, const int32_t* work_list,
                                       int work_items, void* workspace, size_t workspace_bytes,
-                                      void* stream);
+                                      int kv_policy, void* stream);
 /* The shared-prefix pass alone (for timing or scheduling apart): writes the members'
  * partials of the shared partitions into the workspace, and the output row (out, of
  * out_dtype: kv_dtype or PKV_F32) of any member that fits one partition. */
@@ -374,11 +403,14 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, int dtype, const int32_t* src_
  * consecutive entries of tile_ids (device int32 [num_tiles]); entry i names the tile_bytes
  * (a power of two in [256, 1 MiB]) contiguous bytes at tile_ids[i] * tile_bytes of buf (device,
  * 16-byte aligned, buf_bytes long); ids outside the buffer are skipped. Every byte of every
- * listed tile is loaded once. sink (device uint32) is written only if a lane's fold of its
- * loaded words equals sentinel. Enqueued on stream; no synchronisation. */
+ * listed tile is loaded once. flags: 0 for the default cache policy, PKV_PROBE_NONTEMPORAL for
+ * the non-temporal loads that the attention kernels use for KV rows; other bits PKV_EINVAL.
+ * sink (device uint32) is written only if a lane's fold of its loaded words equals sentinel.
+ * Enqueued on stream; no synchronisation. */
+enum { PKV_PROBE_NONTEMPORAL = 1 };
 int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
-                   int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
-                   void* stream);
+                   int num_tiles, int tiles_per_group, int flags, uint32_t sentinel,
+                   uint32_t* sink, void* stream);
 
 /* Per-workgroup timeline of the per-partition decode pass (measurement only; no page defines
  * it). With capacity > 0, every later launch of the per-partition pass (any decode entry

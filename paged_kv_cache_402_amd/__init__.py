@@ -11,7 +11,8 @@ from ._lib import PagedKVError, check, lib, last_error  # noqa: F401  (raises if
 from .block_manager import BlockManager  # noqa: F401
 from .scheduler import Scheduler  # noqa: F401
 from .pool_plan import kv_pool_plan  # noqa: F401
-from .ops import (copy_blocks, decode_work_list, decode_work_list_packed,  # noqa: F401
+from .ops import (KV_CACHED, KV_STREAM, copy_blocks, decode_kv_policy,  # noqa: F401
+                  decode_work_list, decode_work_list_packed,
                   decode_workspace_bytes, decode_workspace_init,
                   default_partition,
                   paged_attention_decode, paged_attention_decode_append,

@@ -23,65 +23,67 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                            c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_float, c_int, c_void_p, c_size_t,
-                                           c_void_p]),
+                                           c_int, c_void_p]),
     "pkv_paged_attention_decode_noalloc": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
                                                    c_void_p, c_int, c_void_p, c_void_p, c_int,
                                                    c_int, c_int, c_int, c_int, c_int, c_int,
-                                                   c_float, c_int, c_void_p]),
+                                                   c_float, c_int, c_int, c_void_p]),
     "pkv_paged_attention_partitions": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                c_int, c_int, c_int, c_int, c_float, c_int,
-                                               c_void_p, c_size_t, c_void_p]),
+                                               c_void_p, c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_reduce": (c_int, [c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "pkv_decode_default_partition": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "pkv_decode_kv_policy": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int, P_i32, c_int,
+                                     c_int]),
     "pkv_decode_work_list": (c_int, [P_i32, c_int, c_int, c_int, c_int, P_i32, c_int]),
     "pkv_decode_work_list_packed": (c_int, [P_i32, c_int, c_int, c_int, c_int, c_int, P_i32,
                                             c_int, P_int]),
     "pkv_paged_attention_decode_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                 c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                 c_int, c_int, c_int, c_int, c_float, c_int,
-                                                c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+                                                c_void_p, c_int, c_void_p, c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_partitions_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
                                                     c_void_p, c_int, c_void_p, c_void_p, c_int,
                                                     c_int, c_int, c_int, c_int, c_int, c_int,
                                                     c_float, c_int, c_void_p, c_int, c_void_p,
-                                                    c_size_t, c_void_p]),
+                                                    c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_decode_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_int, c_void_p, c_void_p,
                                                   c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                                   c_float, c_int, c_void_p, c_int, c_void_p,
-                                                  c_size_t, c_void_p]),
+                                                  c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_partitions_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
                                                       c_void_p, c_void_p, c_void_p, c_int,
                                                       c_void_p, c_void_p, c_int, c_int, c_int,
                                                       c_int, c_int, c_int, c_int, c_float, c_int,
                                                       c_void_p, c_int, c_void_p, c_size_t,
-                                                      c_void_p]),
+                                                      c_int, c_void_p]),
     "pkv_paged_attention_decode_step": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                 c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                                 c_void_p, c_int, c_int, c_int, c_int, c_int,
                                                 c_int, c_int, c_float, c_int, c_void_p, c_int,
-                                                c_void_p, c_size_t, c_void_p]),
+                                                c_void_p, c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_partitions_step": (c_int, [c_void_p, c_int, c_void_p, c_void_p,
                                                     c_void_p, c_void_p, c_void_p, c_void_p,
                                                     c_int, c_void_p, c_void_p, c_int, c_int,
                                                     c_int, c_int, c_int, c_int, c_int, c_float,
                                                     c_int, c_void_p, c_int, c_void_p, c_size_t,
-                                                    c_void_p]),
+                                                    c_int, c_void_p]),
     "pkv_decode_plan_shared_prefix": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
                                               P_i32, P_int, P_int, P_i32, c_int]),
     "pkv_paged_attention_decode_shared": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                   c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                   c_int, c_int, c_int, c_int, c_float, c_int,
                                                   c_void_p, c_int, c_int, c_void_p, c_int,
-                                                  c_void_p, c_size_t, c_void_p]),
+                                                  c_void_p, c_size_t, c_int, c_void_p]),
     "pkv_paged_attention_prefix": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                            c_int, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_int, c_float, c_int, c_void_p, c_int,
                                            c_int, c_void_p, c_size_t, c_void_p]),
     "pkv_debug_timeline": (c_int, [c_void_p, c_int]),
-    "pkv_read_probe": (c_int, [c_void_p, c_size_t, c_int, c_void_p, c_int, c_int,
+    "pkv_read_probe": (c_int, [c_void_p, c_size_t, c_int, c_void_p, c_int, c_int, c_int,
                                ctypes.c_uint32, c_void_p, c_void_p]),
     "pkv_reshape_and_cache": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                       c_int, c_int, c_int, c_int, c_int, c_void_p]),

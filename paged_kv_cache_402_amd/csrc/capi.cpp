@@ -71,8 +71,10 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
                 const void* v_cache, int kv_dtype, const int32_t* block_tables,
                 const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_dim, int block_size, int num_blocks, int max_blocks_per_seq, float scale,
-                int partition_size, void* workspace, size_t workspace_bytes) {
+                int partition_size, void* workspace, size_t workspace_bytes, int kv_policy) {
   if (!dtype_ok(kv_dtype)) return fail(PKV_EDTYPE, "decode: unknown kv dtype %d", kv_dtype);
+  if (kv_policy != PKV_KV_STREAM && kv_policy != PKV_KV_CACHED)
+    return fail(PKV_EINVAL, "decode: unknown kv_policy %d", kv_policy);
   if (out_dtype != kv_dtype && out_dtype != PKV_F32)
     return fail(PKV_EDTYPE, "decode: out dtype must equal the kv dtype or be fp32");
   if (num_seqs < 0 || num_seqs > kMaxGridYZ) return fail(PKV_EINVAL, "decode: num_seqs %d out of range", num_seqs);
@@ -138,6 +140,7 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.cow_src = nullptr;
   a.v_new = nullptr;
   decode_timeline(&a.timeline, &a.timeline_cap);
+  a.kv_cached = kv_policy == PKV_KV_CACHED;
   pl->group = group;
   pl->ws_needed = need;
   return ok();
@@ -167,11 +170,11 @@ int pkv_paged_attention_partitions(void* out, int out_dtype, const void* q, cons
                                    const int32_t* seq_lens, int num_seqs, int num_q_heads,
                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                    int max_blocks_per_seq, float scale, int partition_size,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   void* workspace, size_t workspace_bytes, int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   return hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
                     "decode partitions launch");
@@ -290,6 +293,54 @@ int pkv_decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads
   }
   ok();
   return part;
+}
+
+int pkv_decode_kv_policy(const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                         int max_blocks_per_seq, int block_size, int num_blocks,
+                         const int32_t* work_list, int list_len, int partition_size) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || !is_pow2(block_size) ||
+      (int64_t)max_blocks_per_seq * block_size >= INT32_MAX || list_len < 0)
+    return fail(PKV_EINVAL, "kv_policy: bad sizes");
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "kv_policy: null block_tables or seq_lens");
+  if (work_list != nullptr && (partition_size <= 0 || partition_size % block_size != 0))
+    return fail(PKV_EINVAL, "kv_policy: a work list needs its partition size, a multiple of "
+                "block_size");
+  // block reads of the launch (every in-pool table entry of the tokens it attends, lengths
+  // clamped as the kernel clamps them) against the distinct blocks among them
+  std::vector<uint8_t> seen((size_t)num_blocks, 0);
+  int64_t reads = 0, distinct = 0;
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  auto read_blocks = [&](int b, int64_t t0, int64_t t1) {   // tokens [t0, t1) of sequence b
+    const int32_t* row = block_tables + (size_t)b * max_blocks_per_seq;
+    for (int64_t j = t0 / block_size; j < (t1 + block_size - 1) / block_size; ++j) {
+      const int32_t id = row[j];
+      if (id < 0 || id >= num_blocks) continue;
+      ++reads;
+      if (!seen[id]) {
+        seen[id] = 1;
+        ++distinct;
+      }
+    }
+  };
+  auto length = [&](int b) { return std::min<int64_t>(std::max(seq_lens[b], 0), cap); };
+  if (work_list == nullptr) {
+    for (int b = 0; b < num_seqs; ++b) read_blocks(b, 0, length(b));
+  } else {
+    // plain items (sequence << 16 | partition); packed-row entries (top bit) only point at
+    // items stored further on in the same list, which are counted where they stand
+    for (int i = 0; i < list_len; ++i) {
+      const uint32_t w = (uint32_t)work_list[i];
+      if (w & 0x80000000u) continue;
+      const int b = (int)(w >> 16), p = (int)(w & 0xFFFFu);
+      if (b >= num_seqs) continue;
+      const int64_t t0 = (int64_t)p * partition_size;
+      const int64_t t1 = std::min<int64_t>(t0 + partition_size, length(b));
+      if (t1 > t0) read_blocks(b, t0, t1);
+    }
+  }
+  ok();
+  return reads >= 2 * distinct && reads > 0 ? PKV_KV_CACHED : PKV_KV_STREAM;
 }
 
 int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
@@ -429,11 +480,11 @@ int pkv_paged_attention_partitions_list(void* out, int out_dtype, const void* q,
                                         int head_dim, int block_size, int num_blocks,
                                         int max_blocks_per_seq, float scale, int partition_size,
                                         const int32_t* work_list, int work_items, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+                                        size_t workspace_bytes, int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   return partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
 }
@@ -445,11 +496,11 @@ int pkv_paged_attention_decode_list(void* out, int out_dtype, const void* q, con
                                     int block_size, int num_blocks, int max_blocks_per_seq,
                                     float scale, int partition_size, const int32_t* work_list,
                                     int work_items, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   st = partitions_list(pl, kv_dtype, head_dim, work_list, work_items, stream);
   if (st != PKV_OK || pl.args.pmax <= 1) return st;
@@ -482,11 +533,11 @@ int pkv_paged_attention_decode_append(void* out, int out_dtype, const void* q, c
                                       int num_blocks, int max_blocks_per_seq, float scale,
                                       int partition_size, const int32_t* work_list,
                                       int work_items, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
   st = partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
@@ -503,11 +554,11 @@ int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* 
                                           int max_blocks_per_seq, float scale,
                                           int partition_size, const int32_t* work_list,
                                           int work_items, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
+                                          size_t workspace_bytes, int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
   return partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
@@ -520,11 +571,11 @@ int pkv_paged_attention_decode_step(void* out, int out_dtype, const void* q, con
                                     int num_kv_heads, int head_dim, int block_size,
                                     int num_blocks, int max_blocks_per_seq, float scale,
                                     int partition_size, const int32_t* work_list, int work_items,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    void* workspace, size_t workspace_bytes, int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
   if (!cow_src) return fail(PKV_EINVAL, "decode_step: null cow_src");
@@ -543,11 +594,11 @@ int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
                                         int num_blocks, int max_blocks_per_seq, float scale,
                                         int partition_size, const int32_t* work_list,
                                         int work_items, void* workspace, size_t workspace_bytes,
-                                        void* stream) {
+                                        int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
   if (!cow_src) return fail(PKV_EINVAL, "partitions_step: null cow_src");
@@ -610,7 +661,7 @@ int pkv_paged_attention_prefix(void* out, int out_dtype, const void* q, const vo
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables,
                        seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, scale, partition_size, workspace,
-                       workspace_bytes);
+                       workspace_bytes, PKV_KV_STREAM);
   if (st != PKV_OK || num_seqs == 0) return st;
   return prefix_pass(pl, kv_dtype, head_dim, block_size, members, num_members, prefix_partitions,
                      stream);
@@ -625,11 +676,11 @@ int pkv_paged_attention_decode_shared(void* out, int out_dtype, const void* q,
                                       const int32_t* members, int num_members,
                                       int prefix_partitions, const int32_t* work_list,
                                       int work_items, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   st = prefix_pass(pl, kv_dtype, head_dim, block_size, members, num_members, prefix_partitions,
                    stream);
@@ -684,11 +735,11 @@ int pkv_paged_attention_decode(void* out, int out_dtype, const void* q, const vo
                                const int32_t* seq_lens, int num_seqs, int num_q_heads,
                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                int max_blocks_per_seq, float scale, int partition_size,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, int kv_policy, void* stream) {
   DecodePlan pl;
   int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes);
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
   if (st != PKV_OK || num_seqs == 0) return st;
   st = hip_status(launch_decode_partitions(pl.args, kv_dtype, head_dim, pl.group, (hipStream_t)stream),
                   "decode partitions launch");
@@ -702,14 +753,14 @@ int pkv_paged_attention_decode_noalloc(void* out, int out_dtype, const void* q,
                                        int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_dim, int block_size, int num_blocks,
                                        int max_blocks_per_seq, float scale, int partition_size,
-                                       void* stream) {
+                                       int kv_policy, void* stream) {
   void* ws = nullptr;
   int st = hip_status(static_workspace(&ws), "decode_noalloc: static scratch address");
   if (st != PKV_OK) return st;
   DecodePlan pl;
   st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
                    num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                   max_blocks_per_seq, scale, partition_size, ws, kStaticWorkspaceBytes);
+                   max_blocks_per_seq, scale, partition_size, ws, kStaticWorkspaceBytes, kv_policy);
   if (st == PKV_EWORKSPACE)
     return fail(PKV_EWORKSPACE, "decode_noalloc: these shapes need %zu bytes of split-K scratch; "
                 "the static area holds %zu (use pkv_paged_attention_decode with a workspace, "
@@ -741,8 +792,9 @@ int pkv_debug_timeline(void* buf, int capacity) {
 }
 
 int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int32_t* tile_ids,
-                   int num_tiles, int tiles_per_group, uint32_t sentinel, uint32_t* sink,
-                   void* stream) {
+                   int num_tiles, int tiles_per_group, int flags, uint32_t sentinel,
+                   uint32_t* sink, void* stream) {
+  if (flags & ~PKV_PROBE_NONTEMPORAL) return fail(PKV_EINVAL, "read_probe: unknown flag bits");
   if (!is_pow2(tile_bytes) || tile_bytes < 256 || tile_bytes > (1 << 20))
     return fail(PKV_EINVAL, "read_probe: tile_bytes must be a power of two in [256, 1 MiB]");
   if (num_tiles < 0 || tiles_per_group < 1 || tiles_per_group > 1024)
@@ -760,6 +812,7 @@ int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int3
   a.tile_log2 = log2i(tile_bytes);
   a.sentinel = sentinel;
   a.sink = sink;
+  a.nontemporal = (flags & PKV_PROBE_NONTEMPORAL) != 0;
   return hip_status(launch_read_probe(a, (hipStream_t)stream), "read probe launch");
 }
 

@@ -36,6 +36,11 @@
 //     first round of V loads is issued before this step so it overlaps it;
 //   * V pass: LV lanes (16) own one token row; each lane accumulates p * v for its 8 (or 4)
 //     columns and every head of the group in fp32;
+//   * KV rows are read with the non-temporal cache policy (each row is read once per launch,
+//     and on gfx950 such loads read HBM about 12% faster). Every kernel also exists with
+//     default-policy KV loads, for launches whose sequences mostly read the same blocks
+//     (forks, a long common prefix): there the repeats are served from L2. The caller
+//     chooses per launch (kv_policy); the arithmetic is the same;
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
 //     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence
 //     that fits one partition gets its output row directly, longer ones leave (max, sum,
@@ -124,7 +129,7 @@ template <int N> __device__ __forceinline__ void lds_load_n(const float* src, fl
   }
 }
 
-// Work unit of a workgroup that starts after the first resident round of a work-list launch:
+// Work unit of one of the last workgroups of a work-list launch (the last half machine-full):
 // the next ticket of the scheduling word, in the list's order. Workgroups are dealt to the
 // XCDs round-robin in a fixed share, and XCDs run at slightly different speeds, so a static
 // unit per workgroup leaves the fast XCDs idle at the end of the launch; taken this way, the
@@ -169,9 +174,15 @@ __device__ __forceinline__ uint32_t timeline_now(const DecodeArgs& a) {
   return a.timeline != nullptr ? (uint32_t)__builtin_amdgcn_s_memrealtime() : 0u;
 }
 
-template <int DT, int D, int G, bool MF>
+// NTL: the KV rows are read with the non-temporal cache policy (streaming reads; the default
+// choice), else with the default one (batches whose sequences read the same blocks).
+template <int DT, int D, int G, bool MF, bool NTL>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
   using K = Cfg<DT, D, G>;
+  auto load_kv = [](const unsigned char* p) -> u32x4 {
+    if constexpr (NTL) return load16_stream(p);
+    else return load16(p);
+  };
   constexpr int NW = kDecodeWaves;
   constexpr int NT = kDecodeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -189,8 +200,9 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   if (a.work != nullptr) {
     // unit u is (row u / Hkv, KV head u % Hkv): consecutive units take the KV heads of one
     // row, so with 8 KV heads each XCD of the round-robin dispatch keeps to one head for the
-    // first resident round (a prefix shared by many sequences stays in that XCD's L2); later
-    // workgroups take their units from the scheduling word when there is one
+    // first resident round (a prefix shared by many sequences stays in that XCD's L2); the
+    // last half machine-full of workgroups take their units from the scheduling word when
+    // there is one
     if (a.sched != nullptr && (int)blockIdx.x >= a.sched_static) {
       __shared__ unsigned s_unit;
       if (tid == 0) s_unit = take_unit(a);
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
                                    (uint32_t)(((tok & bs_mask) + rl) * K::RB + kg * 16);
           if (fused && tok + rl == last) p = knew + kg * 16;
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) kb[u][j] = load16(p + j * 64);
+          for (int j = 0; j < NJ; ++j) kb[u][j] = load_kv(p + j * 64);
         } else {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) kb[u][j] = u32x4{0u, 0u, 0u, 0u};
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
                                  (uint32_t)(((tok & bs_mask) + kr) * K::RB + kc * 16);
         if (fused && tok + kr == last) p = knew + kc * 16;
 #pragma unroll
-        for (int i = 0; i < K::NLK; ++i) kv[u][i] = load16(p + i * K::LK * 16);
+        for (int i = 0; i < K::NLK; ++i) kv[u][i] = load_kv(p + i * K::LK * 16);
       } else {
 #pragma unroll
         for (int i = 0; i < K::NLK; ++i) kv[u][i] = u32x4{0u, 0u, 0u, 0u};
@@ -480,7 +492,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
                                  (uint32_t)(((tok & bs_mask) + vr) * K::RB + vc * 16);
         if (fused && tok + vr == last) p = vnew + vc * 16;
 #pragma unroll
-        for (int i = 0; i < K::NLV; ++i) vv[u][i] = load16(p + i * K::LV * 16);
+        for (int i = 0; i < K::NLV; ++i) vv[u][i] = load_kv(p + i * K::LV * 16);
       }
     }
   };
@@ -738,18 +750,21 @@ static int resident_groups(const void* kernel, size_t lds) {
   return groups;
 }
 
-template <int DT, int D, int G, bool MF>
+template <int DT, int D, int G, bool MF, bool NTL>
 static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
-  const auto kernel = paged_decode_partition_kernel<DT, D, G, MF>;
+  const auto kernel = paged_decode_partition_kernel<DT, D, G, MF, NTL>;
   if (a.work != nullptr) {
     const int units = a.num_kv_heads * a.work_items;
-    // Only the last machine-full of units (as many as fit at once) is handed out by ticket:
-    // the list runs longest first, so those are its shortest units, enough to even out the
-    // XCDs' finishing times, while every earlier workgroup keeps its static unit and skips the
-    // ticket's round trip (which a short, latency-bound unit feels).
+    // Only the last half machine-full of units (half as many as fit at once) is handed out
+    // by ticket: the list runs longest first, so those are its shortest units, enough to even
+    // out the XCDs' finishing times. Every earlier workgroup keeps its static unit, and with
+    // it the XCD of its KV head: a unit moved to another XCD reads the blocks its sequences
+    // share (a common prefix) from HBM again instead of that XCD's L2. With non-temporal KV
+    // loads, ticketing a whole machine-full cost more in such re-reads than it saved.
     const int resident = a.sched != nullptr ? resident_groups((const void*)kernel, lds) : 0;
-    if (resident <= 0 || resident >= units) a.sched = nullptr;
-    a.sched_static = units - resident > resident ? units - resident : resident;
+    const int late = resident / 2;
+    a.sched_static = units - late > resident ? units - late : resident;
+    if (late <= 0 || a.sched_static >= units) a.sched = nullptr;
     hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kDecodeThreads), lds, stream, a);
   } else {
     a.sched = nullptr;
@@ -766,8 +781,12 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured
   // faster (the padded 16-row product does 4x the work there and the K pass is not the limit).
   constexpr bool kMF = DT != F32 && G == 8;
-  if (kMF && a.bs_log2 >= 4 && a.part % 64 == 0) return launch_k<DT, D, G, kMF>(a, lds, stream);
-  return launch_k<DT, D, G, false>(a, lds, stream);
+  const bool mf = kMF && a.bs_log2 >= 4 && a.part % 64 == 0;
+  if (a.kv_cached)
+    return mf ? launch_k<DT, D, G, kMF, false>(a, lds, stream)
+              : launch_k<DT, D, G, false, false>(a, lds, stream);
+  return mf ? launch_k<DT, D, G, kMF, true>(a, lds, stream)
+            : launch_k<DT, D, G, false, true>(a, lds, stream);
 }
 
 template <int DT, int D>

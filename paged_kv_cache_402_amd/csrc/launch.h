@@ -50,10 +50,13 @@ struct DecodeArgs {
   // assignment only): {high 32 bits kSchedCookie once initialised, low 32 bits tickets taken}.
   // Workgroups w >= sched_static of the launch take work unit sched_static + ticket instead
   // of unit w, in the list's order, so units go to workgroups in the order they start; the
-  // holder of the last ticket sets the count back to 0. The launch code sets sched_static to
-  // the number of workgroups resident at once.
+  // holder of the last ticket sets the count back to 0. The launch code sets sched_static so
+  // that half as many workgroups as are resident at once take tickets (and at least one
+  // resident round keeps its static units).
   unsigned long long* sched;
   int sched_static;
+  // KV read policy: 0 non-temporal loads (streaming), 1 default cache policy (PKV_KV_CACHED)
+  int kv_cached;
 };
 
 // Bytes of the workspace header that holds the scheduling word.
@@ -129,6 +132,7 @@ struct ProbeArgs {
   int num_tiles, tiles_per_group, tile_log2;
   uint32_t sentinel;
   uint32_t* sink;
+  int nontemporal;           // 1: the non-temporal cache policy of the KV-row loads
 };
 hipError_t launch_read_probe(const ProbeArgs& a, hipStream_t stream);
 

@@ -8,7 +8,9 @@
 // ids are staged in LDS first (as the decode kernel keeps a partition's block ids at hand), then
 // its lanes sweep the tiles' 16-byte vectors in order, eight loads in flight per lane. The
 // loaded words are folded into one value per lane that is stored only if it equals a
-// caller-given sentinel, so no load can be dropped and almost nothing is written.
+// caller-given sentinel, so no load can be dropped and almost nothing is written. The loads
+// take either the default cache policy or the non-temporal one that the attention kernels use
+// for KV rows.
 #include "common.h"
 #include "launch.h"
 
@@ -17,6 +19,7 @@ namespace pkv {
 constexpr int kProbeMaxTiles = 1024;   // tiles per workgroup (ids staged in LDS)
 constexpr int kProbeInFlight = 8;      // 16-byte loads in flight per lane
 
+template <bool NT>
 __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a) {
   __shared__ int s_ids[kProbeMaxTiles];
   const int t0 = blockIdx.x * a.tiles_per_group;
@@ -37,9 +40,11 @@ __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a) {
       v[u] = u32x4{0u, 0u, 0u, 0u};
       if (i < total) {
         const int id = s_ids[i >> shift];
-        if (id >= 0)
-          v[u] = load16(a.buf + ((size_t)id << a.tile_log2) +
-                        ((size_t)(i & ((1 << shift) - 1)) << 4));
+        if (id >= 0) {
+          const unsigned char* p =
+              a.buf + ((size_t)id << a.tile_log2) + ((size_t)(i & ((1 << shift) - 1)) << 4);
+          v[u] = NT ? load16_stream(p) : load16(p);
+        }
       }
     }
 #pragma unroll
@@ -51,7 +56,10 @@ __global__ __launch_bounds__(256) void read_probe_kernel(ProbeArgs a) {
 hipError_t launch_read_probe(const ProbeArgs& a, hipStream_t stream) {
   const int groups = (a.num_tiles + a.tiles_per_group - 1) / a.tiles_per_group;
   if (groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(read_probe_kernel, dim3(groups), dim3(256), 0, stream, a);
+  if (a.nontemporal)
+    hipLaunchKernelGGL(read_probe_kernel<true>, dim3(groups), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(read_probe_kernel<false>, dim3(groups), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -74,6 +74,31 @@ def _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list, shared_p
     return default_partition(B, Hq, Hkv, D, bs, W)
 
 
+KV_STREAM, KV_CACHED = 0, 1   # PKV_KV_STREAM, PKV_KV_CACHED
+
+
+def decode_kv_policy(block_tables, seq_lens, block_size: int, num_blocks: int,
+                     work_list=None, partition_size: int = 0) -> int:
+    """Cache policy for the KV reads of one decode launch (pkv_decode_kv_policy) from host
+    tables [B][W] and lengths [B], over the partitions of the host `work_list` (the whole
+    list, packed or not, built with `partition_size`) or over every token: KV_CACHED when at
+    least half of its block reads repeat a block (forked sequences, a long common prefix),
+    else KV_STREAM."""
+    tab = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if tab.ndim != 2 or lens.shape != (tab.shape[0],):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    wl, n = None, 0
+    if work_list is not None:
+        items = np.ascontiguousarray(np.asarray(work_list, dtype=np.int32).reshape(-1))
+        wl, n = items.ctypes.data_as(P_i32), items.shape[0]
+    return check(lib.pkv_decode_kv_policy(tab.ctypes.data_as(P_i32), lens.ctypes.data_as(P_i32),
+                                          tab.shape[0], tab.shape[1], block_size, num_blocks,
+                                          wl, n, int(partition_size)),
+                 "decode_kv_policy")
+
+
 def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
                      partition_size: int = DEFAULT_PARTITION) -> np.ndarray:
     """Host work list of the per-partition pass (pkv_decode_work_list) from host lengths:
@@ -183,7 +208,7 @@ def _workspace(q, B, Hq, W, bs, D, partition_size, workspace):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
                            partition_size=None, workspace=None, work_list=None,
-                           shared_prefix=None):
+                           shared_prefix=None, kv_policy: int = 0):
     """out[b][h] = softmax(scale * q[b][h] . K_b) V_b over the seq_lens[b] tokens that sequence
     b's block table locates in the paged caches. With work_list (device int32 from
     decode_work_list, or (device list, rows) from decode_work_list_packed) the per-partition
@@ -191,6 +216,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
     (members device int32, prefix_partitions) and the matching work_list (both from
     plan_shared_prefix) the members' shared partitions run in the shared-prefix pass.
     partition_size None picks default_partition's (then no work list may be given).
+    kv_policy: KV_STREAM (non-temporal KV reads) or KV_CACHED (default cache policy), as
+    decode_kv_policy picks it for the batch; speed only, the output is the same.
     Returns `out`."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
@@ -207,25 +234,25 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
         check(lib.pkv_paged_attention_decode_shared(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-            partition_size, mem.data_ptr(), mem.shape[0], int(pp), wl, wn, wsp, wsb, _stream(q)),
+            partition_size, mem.data_ptr(), mem.shape[0], int(pp), wl, wn, wsp, wsb, int(kv_policy), _stream(q)),
             "paged_attention_decode_shared")
     elif work_list is None:
         check(lib.pkv_paged_attention_decode(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-            partition_size, wsp, wsb, _stream(q)), "paged_attention_decode")
+            partition_size, wsp, wsb, int(kv_policy), _stream(q)), "paged_attention_decode")
     else:
         wl, wn = _work(work_list)
         check(lib.pkv_paged_attention_decode_list(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-            partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_decode_list")
+            partition_size, wl, wn, wsp, wsb, int(kv_policy), _stream(q)), "paged_attention_decode_list")
     return out
 
 
 def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
                                partition_size: int = DEFAULT_PARTITION, workspace=None,
-                               work_list=None):
+                               work_list=None, kv_policy: int = 0):
     """First pass of paged_attention_decode only (per-partition attention). Returns the
     workspace that paged_attention_reduce needs (None if no sequence spans two partitions)."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
@@ -236,13 +263,13 @@ def paged_attention_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
         check(lib.pkv_paged_attention_partitions(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-            partition_size, wsp, wsb, _stream(q)), "paged_attention_partitions")
+            partition_size, wsp, wsb, int(kv_policy), _stream(q)), "paged_attention_partitions")
     else:
         wl, wn = _work(work_list)
         check(lib.pkv_paged_attention_partitions_list(
             out.data_ptr(), odt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kdt,
             block_tables.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale),
-            partition_size, wl, wn, wsp, wsb, _stream(q)), "paged_attention_partitions_list")
+            partition_size, wl, wn, wsp, wsb, int(kv_policy), _stream(q)), "paged_attention_partitions_list")
     return ws
 
 
@@ -254,7 +281,8 @@ def _append_args(k_new, v_new, k_cache, B):
 
 
 def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens,
-                                  scale, partition_size=None, workspace=None, work_list=None):
+                                  scale, partition_size=None, workspace=None, work_list=None,
+                                  kv_policy: int = 0):
     """Stores every sequence's newest token (k_new / v_new, [B][Hkv][D], token seq_lens[b] - 1)
     into the caches at the slot its block table gives and decodes, in one pass plus the merge:
     the same caches and bitwise the same output as reshape_and_cache then
@@ -269,14 +297,14 @@ def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_
         out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
         k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
         seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
-        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
         "paged_attention_decode_append")
     return out
 
 
 def paged_attention_partitions_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
                                       seq_lens, scale, partition_size: int = DEFAULT_PARTITION,
-                                      workspace=None, work_list=None):
+                                      workspace=None, work_list=None, kv_policy: int = 0):
     """First pass of paged_attention_decode_append only. Returns the workspace for
     paged_attention_reduce."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
@@ -288,7 +316,7 @@ def paged_attention_partitions_append(out, q, k_new, v_new, k_cache, v_cache, bl
         out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
         k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
         seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
-        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
         "paged_attention_partitions_append")
     return ws
 
@@ -302,7 +330,7 @@ def _cow_arg(cow_src, B):
 
 def paged_attention_decode_step(out, q, k_new, v_new, cow_src, k_cache, v_cache, block_tables,
                                 seq_lens, scale, partition_size=None, workspace=None,
-                                work_list=None):
+                                work_list=None, kv_policy: int = 0):
     """One decode step in one pass plus the merge: each sequence's copy-on-write of its last
     block (cow_src int32 [B]: the source block, or -1), the cache write of its newest token
     (k_new / v_new) and the attention; bitwise copy_blocks, then reshape_and_cache, then
@@ -318,7 +346,7 @@ def paged_attention_decode_step(out, q, k_new, v_new, cow_src, k_cache, v_cache,
         out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
         k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
         seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
-        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
         "paged_attention_decode_step")
     return out
 
@@ -326,7 +354,7 @@ def paged_attention_decode_step(out, q, k_new, v_new, cow_src, k_cache, v_cache,
 def paged_attention_partitions_step(out, q, k_new, v_new, cow_src, k_cache, v_cache,
                                     block_tables, seq_lens, scale,
                                     partition_size: int = DEFAULT_PARTITION, workspace=None,
-                                    work_list=None):
+                                    work_list=None, kv_policy: int = 0):
     """First pass of paged_attention_decode_step only. Returns the workspace for
     paged_attention_reduce."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
@@ -339,7 +367,7 @@ def paged_attention_partitions_step(out, q, k_new, v_new, cow_src, k_cache, v_ca
         out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
         k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
         seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, wl, wn,
-        ws.data_ptr() if ws is not None else None, wsb, _stream(q)),
+        ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
         "paged_attention_partitions_step")
     return ws
 
@@ -417,14 +445,17 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
           "copy_blocks")
 
 
-def read_probe(buf, tile_bytes: int, tile_ids, tiles_per_group: int, sink, sentinel: int = 0x9E3779B9):
+def read_probe(buf, tile_bytes: int, tile_ids, tiles_per_group: int, sink,
+               nontemporal: bool = False, sentinel: int = 0x9E3779B9):
     """Measurement only: reads the tile_bytes tiles of the byte buffer `buf` named by the
-    device int32 `tile_ids`, tiles_per_group of them per 256-lane workgroup (pkv_read_probe).
-    `sink` is a device int32/uint32 tensor of at least one element."""
+    device int32 `tile_ids`, tiles_per_group of them per 256-lane workgroup (pkv_read_probe),
+    with the default or the non-temporal cache policy. `sink` is a device int32/uint32 tensor
+    of at least one element."""
     _dev(buf, "buf")
     _i32(tile_ids, "tile_ids")
     _dev(sink, "sink")
     check(lib.pkv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(tile_bytes),
                              tile_ids.data_ptr(), tile_ids.numel(), int(tiles_per_group),
-                             int(sentinel) & 0xFFFFFFFF, sink.data_ptr(), _stream(buf)),
+                             1 if nontemporal else 0, int(sentinel) & 0xFFFFFFFF,
+                             sink.data_ptr(), _stream(buf)),
           "read_probe")

@@ -491,6 +491,18 @@ def test_decode_step_long_tail_parallel_sampling():
     assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
     assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # the four branches read the same prompt blocks: the policy helper picks the default cache
+    # policy for this batch, and the step under it leaves the same bits
+    assert P.decode_kv_policy(tables, lens, bs, nb) == P.KV_CACHED
+    k3, v3 = kd.clone(), vd.clone()
+    o3 = torch.empty_like(o1)
+    P.paged_attention_decode_step(o3, q, k_new, v_new, i32(cow_src), k3, v3, i32(tables),
+                                  i32(lens), c.scale, partition_size=2048, work_list=work,
+                                  kv_policy=P.KV_CACHED)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k3.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v3.view(torch.uint8))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
 # ------------------------------------------------------------------------------------------

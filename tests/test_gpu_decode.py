@@ -411,9 +411,11 @@ def test_full_size_sampled(which, form):
         tables, lens_d = i32(case.block_tables), i32(case.seq_lens)
         ws = torch.empty(max(1, pk.decode_workspace_bytes(B, Hq, W, bs, D, part)),
                          dtype=torch.uint8, device="cuda")
+        policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, bs, case.num_blocks)
+        assert policy == pk.KV_STREAM          # no batch here mostly re-reads shared blocks
         pk.paged_attention_partitions_append(out, q, k_new, v_new, k, v, tables, lens_d,
                                              case.scale, partition_size=part, workspace=ws,
-                                             work_list=work)
+                                             work_list=work, kv_policy=policy)
         pk.paged_attention_reduce(out, lens_d, bs, W, ws, partition_size=part)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
@@ -438,6 +440,83 @@ def test_full_size_sampled(which, form):
         if odt is not None:
             # the benchmarked rows' magnitudes keep one bf16 rounding inside the 2e-3 bar
             assert max_err(got[s], ref[r]) <= GATE[case.dtype], "seq %d" % s
+
+
+# --------------------------------------------------------------------------------------------
+# the KV read cache policy changes speed only
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("form", ["mha_f16_grid", "gqa_bf16_list_append", "g8_bf16_mfma_grid",
+                                  "f32_g2_packed", "shared_prefix"])
+def test_kv_read_policies_give_the_same_bits(form):
+    """Every decode kernel exists in two builds, non-temporal KV loads and default-policy KV
+    loads (kv_policy). The loaded bytes are the same, so outputs and caches must be bitwise
+    the same; one of the two is checked against the oracle as well."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(7400)
+    grid = form.endswith("grid")
+    if form == "mha_f16_grid":
+        case = gen.make_case("pol1", rng, [1, 31, 700, 2049, 4000], 16, 16, 128, 32, "f16")
+        part, pack = 512, 0
+    elif form == "gqa_bf16_list_append":
+        case = gen.make_case("pol2", rng, [int(x) for x in rng.integers(1, 3000, 40)], 32, 8,
+                             128, 16, "bf16")
+        part, pack = 2048, 0
+    elif form == "g8_bf16_mfma_grid":
+        case = gen.make_case("pol3", rng, [5000, 17, 1536, 3100], 64, 8, 128, 16, "bf16")
+        part, pack = 1536, 0
+    elif form == "f32_g2_packed":
+        case = gen.make_case("pol4", rng, [int(x) for x in rng.integers(1, 200, 60)], 16, 8, 64,
+                             16, "f32")
+        part, pack = 512, 64
+    else:
+        case = _share_case("pol5", 7401, [900, 1300, 700, 2000], 32, 8, 16, "bf16", 512,
+                           [0, 1, 2, 3])
+        part, pack = 256, 0
+    dt, B, Hq, D = case.dtype, case.num_seqs, case.num_q_heads, case.head_dim
+    W, bs, Hkv = case.block_tables.shape[1], case.block_size, case.num_kv_heads
+    tables, lens = i32(case.block_tables), i32(case.seq_lens)
+    q = to_dev(case.q, dt)
+    if grid:
+        work = None
+    elif pack:
+        lst, rows = pk.decode_work_list_packed(case.seq_lens, W, bs, part, pack)
+        work = (i32(lst), rows)
+    else:
+        work = i32(pk.decode_work_list(case.seq_lens, W, bs, part))
+    outs, caches = [], []
+    for policy in (pk.KV_STREAM, pk.KV_CACHED):
+        k, v = to_dev(case.k_cache, dt), to_dev(case.v_cache, dt)
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        if form == "gqa_bf16_list_append":
+            k_new = gen.device_normal((B, Hkv, D), dt, 7402, "cuda")
+            v_new = gen.device_normal((B, Hkv, D), dt, 7403, "cuda")
+            pk.paged_attention_decode_append(out, q, k_new, v_new, k, v, tables, lens, case.scale,
+                                             partition_size=part, work_list=work,
+                                             kv_policy=policy)
+        elif form == "shared_prefix":
+            mem, pp, items = pk.plan_shared_prefix(case.block_tables, case.seq_lens, bs, part)
+            assert pp > 0
+            pk.paged_attention_decode(out, q, k, v, tables, lens, case.scale, partition_size=part,
+                                      work_list=i32(items), shared_prefix=(i32(mem), pp),
+                                      kv_policy=policy)
+        else:
+            pk.paged_attention_decode(out, q, k, v, tables, lens, case.scale, partition_size=part,
+                                      work_list=work, kv_policy=policy)
+        torch.cuda.synchronize()
+        outs.append(out)
+        caches.append((k, v))
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    ib = torch.int32 if dt == "f32" else torch.int16
+    for c0, c1 in zip(caches[0], caches[1]):
+        assert torch.equal(c0.view(ib), c1.view(ib))
+    got = outs[1].cpu().numpy().astype(np.float64)
+    if form == "gqa_bf16_list_append":
+        # the reference reads the caches the pass left (the new rows stored in place)
+        case.k_cache, case.v_cache = to_host(caches[1][0], dt), to_host(caches[1][1], dt)
+    ref = oracle(case)
+    assert np.isfinite(got).all()
+    assert max_err(got, ref) <= GATE[dt]
 
 
 # --------------------------------------------------------------------------------------------

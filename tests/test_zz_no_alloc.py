@@ -37,8 +37,9 @@ def _args(case, out, q, k, v, tables, lens, part):
             case.block_tables.shape[1], ctypes.c_float(case.scale), part)
 
 
-def _both(case, part, out_dtype):
-    """(no-alloc output, workspace output) as float64 host arrays."""
+def _both(case, part, out_dtype, policy):
+    """(no-alloc output, workspace output) as float64 host arrays; policy: the KV read
+    cache policy both calls take."""
     L = _lib()
     dt = case.dtype
     q, k, v = to_dev(case.q, dt), to_dev(case.k_cache, dt), to_dev(case.v_cache, dt)
@@ -49,14 +50,14 @@ def _both(case, part, out_dtype):
     out_ws = torch.full_like(out_na, float("nan"))
     stream = torch.cuda.current_stream().cuda_stream
     st = L.lib.pkv_paged_attention_decode_noalloc(*_args(case, out_na, q, k, v, tables, lens,
-                                                         part), stream)
+                                                         part), policy, stream)
     assert st == 0, L.last_error()
     need = L.lib.pkv_decode_workspace_bytes(B, Hq, case.block_tables.shape[1], case.block_size,
                                             D, part)
     assert 0 < need <= STATIC_BYTES
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     st = L.lib.pkv_paged_attention_decode(*_args(case, out_ws, q, k, v, tables, lens, part),
-                                          ws.data_ptr(), need, stream)
+                                          ws.data_ptr(), need, policy, stream)
     assert st == 0, L.last_error()
     torch.cuda.synchronize()
     return (out_na.float().cpu().numpy().astype(np.float64),
@@ -67,13 +68,13 @@ def test_noalloc_matches_the_workspace_entry_point_on_two_calls():
     rng = np.random.default_rng(7100)
     big = gen.make_case("na1", rng, [int(x) for x in rng.integers(1, 3000, size=24)] + [3000, 1],
                         32, 8, 128, 16, "bf16")
-    got, want = _both(big, 512, "f32")
+    got, want = _both(big, 512, "f32", 0)
     assert np.array_equal(got, want)              # same kernels, same partitions: bitwise
     assert max_err(got, oracle(big)) <= GATE["bf16"]
     # a smaller batch next: the static area still holds the first call's partials
     rng = np.random.default_rng(7101)
     small = gen.make_case("na2", rng, [700, 33, 1500, 512, 0], 8, 8, 64, 32, "f16")
-    got, want = _both(small, 256, "f16")
+    got, want = _both(small, 256, "f16", 1)
     assert np.array_equal(got, want)
     ref = oracle(small)
     assert (np.abs(got - ref) <= out_gate(ref, "f16", "f16")).all()
@@ -92,7 +93,7 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
     lens = torch.full((B,), 100, dtype=torch.int32, device="cuda")
     st = L.lib.pkv_paged_attention_decode_noalloc(
         out.data_ptr(), 2, q.data_ptr(), k.data_ptr(), k.data_ptr(), 2, tables.data_ptr(),
-        lens.data_ptr(), B, Hq, Hkv, D, bs, 8, W, ctypes.c_float(0.1), 512,
+        lens.data_ptr(), B, Hq, Hkv, D, bs, 8, W, ctypes.c_float(0.1), 512, 0,
         torch.cuda.current_stream().cuda_stream)
     assert st == -6 and "static area" in L.last_error()
     torch.cuda.synchronize()
