@@ -425,6 +425,12 @@ def probe_patterns(full):
                  "h's 4 KiB of each; consecutive workgroups differ in head" % nblk))
     pats.append(("gqa_heads_grouped_32KiB", 32 << 10, blocks, 32,
                  "the same %d blocks; one workgroup reads 32 whole blocks" % nblk))
+    # the same 4 KiB tiles as random_4KiB, a quarter of them, each group of 256 read by four
+    # consecutive workgroups: the reuse of blocks that forked sequences share
+    quarter = pats[1][2][: len(pats[1][2]) // 4 // 256 * 256].reshape(-1, 256)
+    pats.append(("shared4_4KiB", 4 << 10, np.repeat(quarter, 4, axis=0).reshape(-1), 256,
+                 "%d of the random 4 KiB tiles, each item of 256 read by 4 consecutive "
+                 "workgroups (bytes counts every read)" % quarter.size))
     pats.append(("random_4KiB_one_per_group", 4 << 10,
                  rng.choice(PROBE_POOL_BYTES >> 12, PROBE_READ_BYTES >> 12, replace=False), 1,
                  "the same bytes as random_4KiB, one tile (4 KiB) per workgroup"))

@@ -171,13 +171,15 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
   // write the transposed V tile to 32 different banks (token pairs 0..15 of two column groups).
   const int vp = tid & 15;
   const int vc = tid >> 4;
+  // default cache policy (not the non-temporal one of the per-partition pass): the other row
+  // chunks of this (KV head, partition) read the same rows, from L2
   auto load_step = [&](int step, u32x4 (&x)[4]) {
     const int tok = step * 32 + 2 * vp;                   // even: tok + 1 is in the same block
     const size_t o0 = row_off(tok) + 16 * vc, o1 = o0 + kRow;
-    x[0] = load16_stream(kbase + o0);
-    x[1] = load16_stream(kbase + o1);
-    x[2] = load16_stream(vbase + o0);
-    x[3] = load16_stream(vbase + o1);
+    x[0] = load16(kbase + o0);
+    x[1] = load16(kbase + o1);
+    x[2] = load16(vbase + o0);
+    x[3] = load16(vbase + o1);
   };
   auto store_step = [&](int buf, const u32x4 (&x)[4]) {
     unsigned char* kd = s_k[buf] + (size_t)(2 * vp) * kKStride + 16 * vc;
