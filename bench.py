@@ -343,7 +343,10 @@ def cpu_baseline(st, target_s, gen):
 # measured HBM traffic of the decode kernel (from rocprofv3 counter runs kept under profiles/)
 # ---------------------------------------------------------------------------------------------
 
-KERNEL_SOURCES = ("paged_kv_cache_402_amd/csrc/decode.hip", "paged_kv_cache_402_amd/csrc/common.h",
+KERNEL_SOURCES = ("paged_kv_cache_402_amd/csrc/decode.hip",
+                  "paged_kv_cache_402_amd/csrc/decode_kernel.h",
+                  "paged_kv_cache_402_amd/csrc/decode_step.hip",
+                  "paged_kv_cache_402_amd/csrc/common.h",
                   "paged_kv_cache_402_amd/csrc/launch.h")
 
 
@@ -856,18 +859,13 @@ def main():
         # the new rows are stored by the decode pass: 2 * B * Hkv * d * eb more bytes written
         bytes_["decode_kernel"] += bytes_["cache_write"] // 2
     if fused_cow:
-        # and the copies: every copied block's rows but the new token's, K and V, written
-        # (their reads are the attention's own, from the source block)
-        eb = {"f32": 4, "f16": 2, "bf16": 2}[case.dtype]
-        row = case.num_kv_heads * case.head_dim * eb
-        bytes_["decode_kernel"] += int(st["pairs"].shape[0]) * 2 * (case.block_size - 1) * row
-        # a copying sequence reads its last block's earlier rows from the source block (which
-        # its siblings list too), not from the copy: those rows of the copy are written, never
-        # read, so they leave the distinct bytes read
+        # the copies: a copying sequence reads its last block's rows before the new token from
+        # the source block (which its siblings list too) and writes them into its copy. The
+        # copy's rows are then written, never read: they leave the distinct bytes read and
+        # enter the bytes written, so the kernel's total stays as counted
         copied = st["cow_src_host"] >= 0
-        skipped = int((st["slots_host"][copied] % case.block_size).sum())
-        bytes_["kv_unique"] -= skipped * case.kv_bytes_per_token()
-        bytes_["decode_kernel"] -= skipped * case.kv_bytes_per_token()
+        copy_rows = int((st["slots_host"][copied] % case.block_size).sum())
+        bytes_["kv_unique"] -= copy_rows * case.kv_bytes_per_token()
     stages = (["copy_blocks"] if st["pairs"] is not None and not fused_cow else []) + \
         ([] if fused else ["reshape_and_cache"]) + \
         (["shared_prefix"] if members is not None and pp > 0 else []) + \

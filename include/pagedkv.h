@@ -293,13 +293,16 @@ int pkv_paged_attention_partitions_append(void* out, int out_dtype, const void* 
  * [num_seqs]) names, for each sequence whose last block the block manager has just made a
  * private copy of (pkv_bm_append_slot returned 1), the block it copied from (cow_src of that
  * call; the table already lists the copy), and -1 for the others; entries outside the pool
- * are ignored. For such a sequence the workgroup of each KV head that holds the new token
- * copies that head's part of the source block into the sequence's last block (every row but
- * the new token's, which it then stores from k_new / v_new), and reads the earlier tokens of
- * that block from the source. Caches and output are bitwise those of pkv_copy_blocks, then
- * pkv_reshape_and_cache, then the decode. Precondition (what a fork gives): in this launch the
- * source block is written only at that same new-token row, by the sequence that kept it.
- * Otherwise as pkv_paged_attention_decode_append. */
+ * are ignored. For such a sequence the pass reads the earlier tokens of that block from the
+ * source, and the workgroup of each KV head stores every such row it reads into the
+ * sequence's last block as it uses it, so the copy costs no loads of its own; the new token's
+ * row comes from k_new / v_new. The output, and every cache row a sequence holds, are bitwise
+ * those of pkv_copy_blocks, then pkv_reshape_and_cache, then the decode; the copied block's
+ * rows past the new token (no token of the sequence is there yet; its next appends write them)
+ * keep what they held, where pkv_copy_blocks would have copied the source's. Precondition
+ * (what a fork gives): in this launch the source block is written only at that same
+ * new-token row, by the sequence that kept it. Otherwise as
+ * pkv_paged_attention_decode_append. */
 int pkv_paged_attention_decode_step(void* out, int out_dtype, const void* q, const void* k_new,
                                     const void* v_new, const int32_t* cow_src, void* k_cache,
                                     void* v_cache, int kv_dtype, const int32_t* block_tables,

@@ -334,7 +334,8 @@ def paged_attention_decode_step(out, q, k_new, v_new, cow_src, k_cache, v_cache,
     """One decode step in one pass plus the merge: each sequence's copy-on-write of its last
     block (cow_src int32 [B]: the source block, or -1), the cache write of its newest token
     (k_new / v_new) and the attention; bitwise copy_blocks, then reshape_and_cache, then
-    paged_attention_decode. Returns `out`."""
+    paged_attention_decode, in the output and every row a sequence holds (a copied block's rows
+    past the new token are left as they were). Returns `out`."""
     B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                       seq_lens)
     partition_size = _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list)

@@ -86,6 +86,19 @@ def test_copy_blocks_skips_pairs_outside_the_pool():
     assert _bits_equal(kd, kr, "f32")
 
 
+def _fused_copy_expected(apart, before, pairs, slots, bs):
+    """The caches a one-pass decode step leaves: those of copy_blocks then reshape_and_cache
+    (`apart`), except that in each copied block the rows past the new token's keep what the
+    block held before the step (`before`): the fused copy writes the rows the sequence holds,
+    the block's earlier rows, and no row past its new token."""
+    want = apart.clone() if hasattr(apart, "clone") else apart.copy()
+    new_row = {int(x) // bs: int(x) % bs for x in np.asarray(slots).reshape(-1)}
+    for _, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        r = new_row[dst]
+        want[dst, :, r + 1:] = before[dst, :, r + 1:]
+    return want
+
+
 def _hash_blocks(pool_dev, dtype):
     h = to_host(pool_dev, dtype)
     return [hashlib.sha256(np.ascontiguousarray(h[b]).tobytes()).hexdigest() for b in range(h.shape[0])]
@@ -313,11 +326,15 @@ def test_beam_search_loop_decodes_every_step(width, part, fused):
         if fused:
             out = torch.full((len(seqs), Hq, d), float("nan"), dtype=torch.float32,
                              device="cuda")
+            kb, vb = to_host(kd, dt), to_host(vd, dt)
             P.paged_attention_decode_step(out, to_dev(q, dt), to_dev(nk, dt), to_dev(nv, dt),
                                           i32(cow_src), kd, vd, i32(tables), i32(lens), 0.0884,
                                           partition_size=part)
             torch.cuda.synchronize()
             got = out.cpu().numpy().astype(np.float64)
+            # rows of a copied block past the new token are not copied by the fused step
+            host_k = _fused_copy_expected(host_k, kb, ref_pairs, sl, bs)
+            host_v = _fused_copy_expected(host_v, vb, ref_pairs, sl, bs)
         else:
             got, _ = run_decode(case, k=kd, v=vd, partition_size=part)
         worst = max(worst, max_err(got, oracle(case)))
@@ -448,8 +465,10 @@ def test_decode_step_is_copy_then_cache_write_then_decode(dtype, hq, hkv, bs, pa
     P.paged_attention_decode_step(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
                                   i32(lens), scale, partition_size=part, work_list=work)
     torch.cuda.synchronize()
-    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
-    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    want_k = _fused_copy_expected(k1, kd, pairs, slots, bs)
+    want_v = _fused_copy_expected(v1, vd, pairs, slots, bs)
+    assert torch.equal(want_k.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(want_v.view(torch.uint8), v2.view(torch.uint8))
     assert torch.equal(o1, o2)
     ref = gen.PagedDecodeCase("step", dtype, hq, hkv, d, bs, nb, lens, tables, scale,
                               q=to_host(q, dtype), k_cache=to_host(k2, dtype),
@@ -488,8 +507,10 @@ def test_decode_step_long_tail_parallel_sampling():
     P.paged_attention_decode_step(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
                                   i32(lens), c.scale, partition_size=2048, work_list=work)
     torch.cuda.synchronize()
-    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
-    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    want_k = _fused_copy_expected(k1, kd, pairs, slots, bs)
+    want_v = _fused_copy_expected(v1, vd, pairs, slots, bs)
+    assert torch.equal(want_k.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(want_v.view(torch.uint8), v2.view(torch.uint8))
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     # the four branches read the same prompt blocks: the policy helper picks the default cache
     # policy for this batch, and the step under it leaves the same bits
@@ -500,8 +521,8 @@ def test_decode_step_long_tail_parallel_sampling():
                                   i32(lens), c.scale, partition_size=2048, work_list=work,
                                   kv_policy=P.KV_CACHED)
     torch.cuda.synchronize()
-    assert torch.equal(k1.view(torch.uint8), k3.view(torch.uint8))
-    assert torch.equal(v1.view(torch.uint8), v3.view(torch.uint8))
+    assert torch.equal(k2.view(torch.uint8), k3.view(torch.uint8))
+    assert torch.equal(v2.view(torch.uint8), v3.view(torch.uint8))
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
