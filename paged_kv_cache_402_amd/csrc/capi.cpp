@@ -307,8 +307,16 @@ int pkv_decode_kv_policy(const int32_t* block_tables, const int32_t* seq_lens, i
     return fail(PKV_EINVAL, "kv_policy: a work list needs its partition size, a multiple of "
                 "block_size");
   // block reads of the launch (every in-pool table entry of the tokens it attends, lengths
-  // clamped as the kernel clamps them) against the distinct blocks among them
-  std::vector<uint8_t> seen((size_t)num_blocks, 0);
+  // clamped as the kernel clamps them) against the distinct blocks among them. A block was
+  // seen in this call when its stamp equals this call's; the stamps persist per thread, so a
+  // call costs O(reads) and not a pass over the whole pool.
+  thread_local std::vector<uint32_t> stamp;
+  thread_local uint32_t epoch = 0;
+  if (stamp.size() < (size_t)num_blocks) stamp.resize((size_t)num_blocks, 0);
+  if (++epoch == 0) {                       // wrapped: forget every stamp
+    std::fill(stamp.begin(), stamp.end(), 0u);
+    epoch = 1;
+  }
   int64_t reads = 0, distinct = 0;
   const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
   auto read_blocks = [&](int b, int64_t t0, int64_t t1) {   // tokens [t0, t1) of sequence b
@@ -317,8 +325,8 @@ int pkv_decode_kv_policy(const int32_t* block_tables, const int32_t* seq_lens, i
       const int32_t id = row[j];
       if (id < 0 || id >= num_blocks) continue;
       ++reads;
-      if (!seen[id]) {
-        seen[id] = 1;
+      if (stamp[id] != epoch) {
+        stamp[id] = epoch;
         ++distinct;
       }
     }
