@@ -91,12 +91,6 @@ __global__ __launch_bounds__(256) void paged_decode_reduce_kernel(DecodeArgs a) 
   }
 }
 
-size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part) {
-  (void)kv_dtype;
-  // per wave: its scores (part / 4 x group floats), reused for its merge data afterwards
-  const int per = part / kDecodeWaves > head_dim + 2 ? part / kDecodeWaves : head_dim + 2;
-  return (size_t)kDecodeWaves * (size_t)per * (size_t)group * 4;
-}
 
 int resident_groups(const void* kernel, size_t lds) {
   struct Entry {

@@ -14,6 +14,10 @@ constexpr int kDecodeWaves = 4;
 // Work-list row flag: the row (flag | idx) stands for the four items stored at idx .. idx + 3
 // of the list, one per wave of the workgroup.
 constexpr uint32_t kPackedRow = 0x80000000u;
+// Shared-prefix pass: the head_dim it is built for, and the block ids of one partition it
+// keeps in LDS.
+constexpr int kPrefixHeadDim = 128;
+constexpr int kPrefixMaxIds = 256;
 
 struct DecodeArgs {
   void* out;                   // [B][Hq][D] of out dtype

@@ -83,11 +83,11 @@ __device__ __forceinline__ float row4_max(float x) {
 
 constexpr float kRescaleSlack = 8.f;      // log2 units a row's max may pass its reference
 
-constexpr int kD = 128;                   // head_dim of this pass
+constexpr int kD = kPrefixHeadDim;        // head_dim of this pass
 constexpr int kRow = kD * 2;              // bytes of one token row of one head
 constexpr int kVtStride = 32 * 2 + 8;     // bytes of one V^T row in LDS (32 tokens + pad)
 constexpr int kKStride = kRow + 16;       // bytes of one K row in LDS (padded)
-constexpr int kMaxIds = 256;              // block ids of one partition kept in LDS
+constexpr int kMaxIds = kPrefixMaxIds;    // block ids of one partition kept in LDS
 
 }  // namespace
 
@@ -324,13 +324,6 @@ __global__ __launch_bounds__(256) void paged_prefix_kernel(PrefixArgs a) {
   }
 }
 
-bool prefix_supported(int kv_dtype, int head_dim, int group, int part, int bs_log2) {
-  return (kv_dtype == BF16 || kv_dtype == F16) && head_dim == kD &&
-         (group == 1 || group == 2 || group == 4 || group == 8) && part % 32 == 0 &&
-         (part >> bs_log2) <= kMaxIds;
-}
-
-int prefix_chunk_seqs(int group) { return 4 * (16 / group); }
 
 template <int DT, int G>
 static void launch_pf(const PrefixArgs& a, dim3 grid, hipStream_t stream) {
