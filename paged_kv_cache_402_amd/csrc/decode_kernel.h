@@ -41,6 +41,10 @@
 //     default-policy KV loads, for launches whose sequences mostly read the same blocks
 //     (forks, a long common prefix): there the repeats are served from L2. The caller
 //     chooses per launch (kv_policy); the arithmetic is the same;
+//   * optional fusions of the decode step: the newest token's K/V rows come from k_new /
+//     v_new and are stored into the cache slot; and a copy-on-write of the last block is
+//     made by storing the source rows the passes read into the private copy as they are
+//     used (only in the kernels built for launches with copy sources, decode_step.hip);
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
 //     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence
 //     that fits one partition gets its output row directly, longer ones leave (max, sum,
@@ -56,7 +60,6 @@
 #include "launch.h"
 
 namespace pkv {
-
 
 template <int DT, int D, int G>
 struct Cfg {
