@@ -913,6 +913,13 @@ def main():
     def new_events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
+    # The read probe (achievable bandwidth) runs before the warm-up steps: it also keeps the GPU
+    # busy long enough for its clocks to settle, which the few warm-up steps alone do not (run
+    # after the timed steps, the probe left the first timed steps up to 8% slower than the rest).
+    probe = None
+    if not args.no_read_probe:
+        log("read probe (achievable read bandwidth)")
+        probe = read_probe(pk, torch, dev, full=False)
     log("warmup %d" % W)
     for _ in range(W):
         step()
@@ -1018,9 +1025,7 @@ def main():
                               "step's fraction is frac_of_hbm_peak",
                      "bytes_per_launch": kernel_bytes},
     }
-    if not args.no_read_probe:
-        log("read probe (achievable read bandwidth)")
-        probe = read_probe(pk, torch, dev, full=False)
+    if probe is not None:
         ach = probe_rate(probe, "stream_2GiB", "nontemporal")
         result["achievable_GBps"] = ach
         result["achievable_note"] = ("2 GiB streaming read with the KV loads' non-temporal "
