@@ -222,10 +222,14 @@ int pkv_decode_work_list(const int32_t* seq_lens, int num_seqs, int max_blocks_p
  * bound (a chain of dependent loads), so the launch shortens. Layout: *rows entries first,
  * each a plain item or a packed row 0x80000000 | idx naming the four items stored at
  * idx .. idx + 3 further on in the list (a last, partial group is padded with items naming
- * sequence 0xFFFF, which every launch skips). Pass the whole list and work_items = *rows to
- * the _list and _append entry points. A packed wave computes its partition alone, so those
- * outputs equal the four-wave ones up to fp32 rounding order, not bitwise. Returns the list
- * length (with work_list NULL: a size query, *rows still set); negative on bad arguments. */
+ * sequence 0xFFFF, which every launch skips). The short items are grouped in the plain list's
+ * order (longest first); the rows run in decreasing order of the tokens one wave of the row
+ * takes: a plain item's tokens / 4 rounded up, a packed row's longest item (ties in list
+ * order, plain rows first), so the rows that take longest start first. Pass the whole list
+ * and work_items = *rows to the _list and _append entry points. A packed wave computes its
+ * partition alone, so those outputs equal the four-wave ones up to fp32 rounding order, not
+ * bitwise. Returns the list length (with work_list NULL: a size query, *rows still set);
+ * negative on bad arguments. */
 int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_blocks_per_seq,
                                 int block_size, int partition_size, int pack_tokens,
                                 int32_t* work_list, int capacity, int* rows);
@@ -421,7 +425,8 @@ int pkv_read_probe(const void* buf, size_t buf_bytes, int tile_bytes, const int3
  * and end time (s_memrealtime, a 100 MHz clock, low 32 bits), the HW_ID register (CU, SIMD
  * and shader-engine ids), the XCC_ID register (XCD), the work unit it took (work-list
  * launches: row * num_kv_heads + KV head; else w), the times its first wave finished its key
- * pass and its value pass, and the tokens of its partition, from the workgroup's first lane. Workgroups that find no work (list entries past a sequence's end) write nothing, so
+ * pass and its value pass, and the tokens of its partition, from the workgroup's first
+ * lane. Workgroups that find no work (list entries past a sequence's end) write nothing, so
  * clear the buffer first. buf: device, 16-byte aligned, 32 * capacity bytes, owned by the
  * caller and kept alive until the timeline is switched off with capacity 0. Process-wide;
  * not for concurrent use with launches on other threads. */

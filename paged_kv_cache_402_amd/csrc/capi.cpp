@@ -227,10 +227,14 @@ std::vector<uint32_t> build_work_list(const int32_t* seq_lens, int num_seqs, int
   return full;
 }
 
-// Rows of a packed list: the items of more than pack_tokens tokens as they are, then one
-// row (kPackedRow | idx) per four consecutive shorter items, which are stored after the rows
-// from index idx (the last group padded with items naming sequence 0xFFFF, which every
-// launch skips). items are in build_work_list order, so the short ones are its tail.
+// Rows of a packed list: each item of more than pack_tokens tokens as a row of its own, and
+// one row (kPackedRow | idx) per four consecutive shorter items, which are stored after the
+// rows from index idx (the last group padded with items naming sequence 0xFFFF, which every
+// launch skips). items are in build_work_list order, so the short ones are its tail, longest
+// first. The rows run in decreasing order of the tokens one wave of the row goes through:
+// a plain item's four waves share its tokens, a packed wave takes its whole item, so a packed
+// row weighs as much as its longest item and a plain one a quarter of its tokens (ties: list
+// order, plain rows first). The launch then starts the rows that take longest first.
 std::vector<uint32_t> pack_work_list(const std::vector<uint32_t>& items, const int32_t* seq_lens,
                                      int64_t cap_tokens, int partition_size, int pack_tokens,
                                      int* rows) {
@@ -242,9 +246,20 @@ std::vector<uint32_t> pack_work_list(const std::vector<uint32_t>& items, const i
   while (first > 0 && tokens(items[first - 1]) <= pack_tokens) --first;
   const size_t nshort = items.size() - first;
   const size_t groups = (nshort + 3) / 4;
-  std::vector<uint32_t> out(items.begin(), items.begin() + (long)first);
   const size_t base = first + groups;
-  for (size_t g = 0; g < groups; ++g) out.push_back(kPackedRow | (uint32_t)(base + 4 * g));
+  std::vector<std::pair<int64_t, uint32_t>> keyed;   // (-tokens per wave, row)
+  keyed.reserve(base);
+  for (size_t i = 0; i < first; ++i)
+    keyed.emplace_back(-((tokens(items[i]) + kDecodeWaves - 1) / kDecodeWaves), items[i]);
+  for (size_t g = 0; g < groups; ++g)
+    keyed.emplace_back(-tokens(items[first + 4 * g]), kPackedRow | (uint32_t)(base + 4 * g));
+  std::stable_sort(keyed.begin(), keyed.end(),
+                   [](const std::pair<int64_t, uint32_t>& x, const std::pair<int64_t, uint32_t>& y) {
+                     return x.first < y.first;
+                   });
+  std::vector<uint32_t> out;
+  out.reserve(base + 4 * groups);
+  for (const auto& k : keyed) out.push_back(k.second);
   *rows = (int)out.size();
   for (size_t i = 0; i < 4 * groups; ++i)
     out.push_back(i < nshort ? items[first + i] : 0xFFFF0000u);

@@ -74,9 +74,11 @@ def unpack(lst, rows):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_packed_work_list_matches_definition(seed):
-    """The packed list holds the plain list's items in the same order: the items of more than
-    pack_tokens tokens one per row, then the rest four per row (the last row padded with
-    sequence 0xFFFF), every stored item referenced by exactly one row."""
+    """The packed list holds the plain list's items: the items of more than pack_tokens tokens
+    one per row, the rest four per row in the plain list's order (the last row padded with
+    sequence 0xFFFF), every stored item referenced by exactly one row; the rows sorted by the
+    tokens one of their waves takes (a plain item's tokens / 4 rounded up, a packed row's
+    longest item), most first, ties in list order with plain rows first."""
     import paged_kv_cache_402_amd as pk
     rng = np.random.default_rng(100 + seed)
     bs = int(rng.choice([8, 16, 64]))
@@ -93,15 +95,22 @@ def test_packed_work_list_matches_definition(seed):
         for p in range(max(1, -(-L // part))):
             ntok[(b, p)] = min(part, L - p * part)
     nshort = sum(1 for it in plain if ntok[it] <= pack)
-    single = [r for r in got if len(r) == 1]
-    groups = [r for r in got if len(r) == 4]
-    assert len(single) + len(groups) == rows and got[:len(single)] == single
-    assert [r[0] for r in single] == plain[:len(plain) - nshort]
-    flat = [it for r in groups for it in r]
-    assert flat[:nshort] == plain[len(plain) - nshort:]
-    assert all(it == (0xFFFF, 0) for it in flat[nshort:]) and len(flat) - nshort < 4
-    assert len(lst) == rows + len(flat)
-    assert all(ntok[it] > pack for it in plain[:len(plain) - nshort])
+    long_items = plain[:len(plain) - nshort]
+    assert all(ntok[it] > pack for it in long_items)
+    short = plain[len(plain) - nshort:]
+    pad = (-nshort) % 4
+    stored = short + [(0xFFFF, 0)] * pad
+    groups = [stored[i:i + 4] for i in range(0, len(stored), 4)]
+    # rows as the definition orders them: (weight, plain first, position in the list)
+    keyed = [(-(-ntok[it] // 4), 0, i, [it]) for i, it in enumerate(long_items)]
+    keyed += [(ntok[g[0]], 1, i, g) for i, g in enumerate(groups)]
+    want = [row for _, _, _, row in sorted(keyed, key=lambda k: (-k[0], k[1], k[2]))]
+    assert rows == len(want) and got == want
+    # the groups are stored in order right after the rows, each referenced once
+    u = np.asarray(lst, dtype=np.int32).view(np.uint32)
+    refs = sorted(int(r & 0x7FFFFFFF) for r in u[:rows] if r & 0x80000000)
+    assert refs == [rows + 4 * g for g in range(len(groups))]
+    assert len(lst) == rows + 4 * len(groups)
     # pack_tokens 0: the plain list, every entry a row
     lst0, rows0 = pk.decode_work_list_packed(lens, width, bs, part, 0)
     assert rows0 == len(lst0) and decode(lst0) == plain
