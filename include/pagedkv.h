@@ -329,6 +329,63 @@ int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
                                         int kv_policy, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Fork groups (P2 §2.2: the branches of a parallel-sampling fork share their prompt's blocks
+ * until each writes its own token; P1 §6.2 copy-on-write). Right after a fork, every branch
+ * attends to the same tokens before its own new one. A fork group lists such sequences: the
+ * same length, the same table entries before the new token's block, and, for the earlier rows
+ * of that block, the same block to read them from (the block the copies were made from, or
+ * the block itself for the branch that kept it). The step then reads those tokens once per
+ * group and KV head, for every member's query heads at once, instead of once per member.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Host planner, from host copies of the tables, lengths and copy sources (cow_src may be NULL:
+ * no copies): the runs of sequences with equal keys (length; table entries before the new
+ * token's block; the block the new token's block reads its earlier rows from, which is
+ * cow_src[b] when it names a pool block, else the table's entry, and none when the new token
+ * opens its block), in increasing sequence order, cut into groups of at most group_size.
+ * groups (capacity x group_size int32) receives them, -1 filling a short group, and
+ * group_lens (capacity int32) their length; the groups are ordered by their first member. A
+ * sequence of length 0 is a group of its own. With groups and group_lens NULL returns the
+ * group count; otherwise writes them (capacity >= count, else PKV_EINVAL) and returns the
+ * count. Negative on bad arguments. The work list over the groups is pkv_decode_work_list
+ * (or _packed) of group_lens. */
+int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_lens,
+                                const int32_t* cow_src, int num_seqs, int max_blocks_per_seq,
+                                int block_size, int num_blocks, int group_size, int32_t* groups,
+                                int32_t* group_lens, int capacity);
+
+/* pkv_paged_attention_decode_step over fork groups: groups (device int32
+ * [num_groups][group_size], from pkv_decode_plan_fork_groups or a caller that knows its forks;
+ * -1 marks an empty place) and a work list whose items name groups (pkv_decode_work_list or
+ * _packed of the groups' lengths; required). group_size x (num_q_heads / num_kv_heads) must be
+ * 1, 2, 4 or 8 (8 only up to head_dim 128). Each workgroup reads the group's shared tokens
+ * through its first member's table, scores them against every member's query heads, adds
+ * each member's own new token from k_new / v_new, stores each member's new K and V rows into
+ * its own block, and stores the earlier rows of the new token's block into the copy of every
+ * member whose cow_src names a source (cow_src may be NULL: no copies). Outputs, and every
+ * cache row a sequence holds, are those of pkv_paged_attention_decode_step on the same
+ * arguments: the cache rows bitwise, the outputs up to fp32 rounding order (the own token is
+ * added after the shared ones). Sequences in no group get no output. num_seqs and num_groups
+ * are at most 32767. */
+int pkv_paged_attention_decode_step_groups(
+    void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
+    const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+    float scale, int partition_size, const int32_t* groups, int num_groups, int group_size,
+    const int32_t* work_list, int work_items, void* workspace, size_t workspace_bytes,
+    int kv_policy, void* stream);
+/* Its per-partition pass alone (the merge is pkv_paged_attention_reduce). */
+int pkv_paged_attention_partitions_step_groups(
+    void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
+    const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+    float scale, int partition_size, const int32_t* groups, int num_groups, int group_size,
+    const int32_t* work_list, int work_items, void* workspace, size_t workspace_bytes,
+    int kv_policy, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Shared-prefix decode (P1 §6.1; P3 §2.2.3, §2.2.8: sequences that start with the same
  * prompt list the same physical blocks). The leading partitions that a group of sequences
  * shares are attended once per (KV head, partition) for all the group's query rows, as

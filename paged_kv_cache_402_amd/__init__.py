@@ -17,6 +17,8 @@ from .ops import (KV_CACHED, KV_STREAM, copy_blocks, decode_kv_policy,  # noqa: 
                   default_partition,
                   paged_attention_decode, paged_attention_decode_append,
                   paged_attention_decode_step, paged_attention_partitions_step,
+                  paged_attention_decode_step_groups, paged_attention_partitions_step_groups,
+                  plan_fork_groups,
                   paged_attention_partitions, paged_attention_partitions_append,
                   paged_attention_prefix,
                   paged_attention_reduce, plan_shared_prefix, read_probe,

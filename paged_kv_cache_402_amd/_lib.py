@@ -6,6 +6,12 @@ if the library is missing, importing this module raises.
 import ctypes
 import os
 
+# torch before the library: the torch wheel carries its own HIP runtime, and libpagedkv.so must
+# bind to the runtime torch already loaded. Loaded first, the library would pull in the system
+# one instead, and a process holding two HIP runtimes gets "no ROCm-capable device" from
+# whichever initialises second.
+import torch  # noqa: F401,E402
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 c_int, c_int64, c_size_t, c_float = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -71,6 +77,18 @@ SIGNATURES = {
                                                     c_int, c_int, c_int, c_int, c_int, c_float,
                                                     c_int, c_void_p, c_int, c_void_p, c_size_t,
                                                     c_int, c_void_p]),
+    "pkv_decode_plan_fork_groups": (c_int, [P_i32, P_i32, P_i32, c_int, c_int, c_int, c_int,
+                                            c_int, P_i32, P_i32, c_int]),
+    "pkv_paged_attention_decode_step_groups": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                c_float, c_int, c_void_p, c_int, c_int, c_void_p,
+                                                c_int, c_void_p, c_size_t, c_int, c_void_p]),
+    "pkv_paged_attention_partitions_step_groups": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                c_float, c_int, c_void_p, c_int, c_int, c_void_p,
+                                                c_int, c_void_p, c_size_t, c_int, c_void_p]),
     "pkv_decode_plan_shared_prefix": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
                                               P_i32, P_int, P_int, P_i32, c_int]),
     "pkv_paged_attention_decode_shared": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpagedkv.so")
 
-SOURCES = ["decode.hip", "decode_step.hip", "prefix.hip", "cache_ops.hip", "probe.hip", "static_ws.hip", "capi.cpp", "shapes.cpp", "block_manager.cpp",
+SOURCES = ["decode.hip", "decode_step.hip", "decode_groups.hip", "prefix.hip", "cache_ops.hip",
+           "probe.hip", "static_ws.hip", "capi.cpp", "shapes.cpp", "block_manager.cpp",
            "scheduler.cpp", "pool_plan.cpp", "errors.cpp"]
 ARCH = "gfx950"
 

@@ -141,6 +141,10 @@ int plan_decode(DecodePlan* pl, void* out, int out_dtype, const void* q, const v
   a.v_new = nullptr;
   decode_timeline(&a.timeline, &a.timeline_cap);
   a.kv_cached = kv_policy == PKV_KV_CACHED;
+  a.groups = nullptr;
+  a.num_groups = 0;
+  a.group_size = 1;
+  a.group_heads = group;
   pl->group = group;
   pl->ws_needed = need;
   return ok();
@@ -407,6 +411,82 @@ int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_b
   return st;
 }
 
+int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_lens,
+                                const int32_t* cow_src, int num_seqs, int max_blocks_per_seq,
+                                int block_size, int num_blocks, int group_size, int32_t* groups,
+                                int32_t* group_lens, int capacity) {
+  if (num_seqs < 0 || num_seqs > kMaxListSeqs)
+    return fail(PKV_EINVAL, "plan_fork_groups: num_seqs %d out of range [0, %d]", num_seqs,
+                kMaxListSeqs);
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_EINVAL, "plan_fork_groups: block_size must be a power of two in [8, 256]");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size >= INT32_MAX)
+    return fail(PKV_EINVAL, "plan_fork_groups: max_blocks_per_seq out of range");
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "plan_fork_groups: num_blocks must be positive");
+  if (group_size < 1) return fail(PKV_EINVAL, "plan_fork_groups: group_size must be >= 1");
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "plan_fork_groups: null tables or seq_lens");
+  const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+  const int shift = log2i(block_size);
+  struct Key {
+    int64_t len;     // clamped length, the new token included
+    int64_t blocks;  // blocks before the new token's block
+    int src;         // block its earlier rows come from (-1: none)
+  };
+  std::vector<Key> key(num_seqs);
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t L = std::min<int64_t>(std::max(seq_lens[b], 0), cap_tokens);
+    Key k{L, L > 0 ? (L - 1) >> shift : 0, -1};
+    if (L > 0 && ((L - 1) & (block_size - 1)) != 0) {
+      const int c = cow_src ? cow_src[b] : -1;
+      k.src = (unsigned)c < (unsigned)num_blocks
+                  ? c
+                  : block_tables[(size_t)b * max_blocks_per_seq + (size_t)k.blocks];
+    }
+    key[b] = k;
+  }
+  auto row = [&](int b) { return block_tables + (size_t)b * max_blocks_per_seq; };
+  auto less = [&](int x, int y) {
+    const Key &a = key[x], &b = key[y];
+    if (a.len != b.len) return a.len < b.len;
+    if (a.src != b.src) return a.src < b.src;
+    return std::lexicographical_compare(row(x), row(x) + a.blocks, row(y), row(y) + b.blocks);
+  };
+  auto same = [&](int x, int y) {
+    // a sequence of length 0 attends to nothing and shares with nobody
+    return key[x].len > 0 && !less(x, y) && !less(y, x);
+  };
+  std::vector<int> order(num_seqs);
+  for (int b = 0; b < num_seqs; ++b) order[b] = b;
+  std::stable_sort(order.begin(), order.end(), less);
+  // runs of equal keys (in increasing sequence order), in chunks of group_size
+  std::vector<std::vector<int>> out;
+  for (size_t i = 0; i < order.size();) {
+    size_t j = i + 1;
+    while (j < order.size() && same(order[i], order[j])) ++j;
+    for (size_t c = i; c < j; c += (size_t)group_size)
+      out.emplace_back(order.begin() + (long)c, order.begin() + (long)std::min(j, c + group_size));
+    i = j;
+  }
+  std::sort(out.begin(), out.end(), [](const std::vector<int>& x, const std::vector<int>& y) {
+    return x[0] < y[0];
+  });
+  const int n = (int)out.size();
+  if (!groups && !group_lens) {   // size query
+    ok();
+    return n;
+  }
+  if (!groups || !group_lens) return fail(PKV_EINVAL, "plan_fork_groups: null output");
+  if (capacity < n) return fail(PKV_EINVAL, "plan_fork_groups: %d groups, capacity %d", n, capacity);
+  for (int g = 0; g < n; ++g) {
+    for (int j = 0; j < group_size; ++j)
+      groups[(size_t)g * group_size + j] = j < (int)out[g].size() ? out[g][j] : -1;
+    group_lens[g] = (int32_t)key[out[g][0]].len;
+  }
+  ok();
+  return n;
+}
+
 int pkv_decode_plan_shared_prefix(const int32_t* block_tables, const int32_t* seq_lens,
                                   int num_seqs, int max_blocks_per_seq, int block_size,
                                   int partition_size, int min_members, int32_t* members,
@@ -627,6 +707,78 @@ int pkv_paged_attention_partitions_step(void* out, int out_dtype, const void* q,
   if (!cow_src) return fail(PKV_EINVAL, "partitions_step: null cow_src");
   pl.args.cow_src = cow_src;
   return partitions_any(pl, kv_dtype, head_dim, work_list, work_items, stream);
+}
+
+// The per-partition pass of a one-pass step over fork groups: work items name groups.
+static int groups_pass(const DecodePlan& pl0, int kv_dtype, int head_dim, const int32_t* cow_src,
+                       const int32_t* groups, int num_groups, int group_size,
+                       const int32_t* work_list, int work_items, void* stream) {
+  if (group_size < 1 || num_groups < 0 || work_items < 0)
+    return fail(PKV_EINVAL, "step_groups: bad group_size, num_groups or work_items");
+  const int64_t rows = (int64_t)group_size * pl0.group;
+  if (rows != 1 && rows != 2 && rows != 4 && rows != 8)
+    return fail(PKV_EINVAL, "step_groups: group_size x query heads per KV head must be 1, 2, 4 "
+                "or 8 (got %lld)", (long long)rows);
+  if (rows == 8 && head_dim > 128)
+    return fail(PKV_EINVAL, "step_groups: 8 rows need head_dim <= 128");
+  if (num_groups > kMaxListSeqs)
+    return fail(PKV_EINVAL, "step_groups: at most %d groups", kMaxListSeqs);
+  if (pl0.args.num_seqs > kMaxListSeqs)
+    return fail(PKV_EINVAL, "step_groups: at most %d sequences", kMaxListSeqs);
+  if (num_groups == 0 || work_items == 0) return ok();
+  if (!groups || !work_list) return fail(PKV_EINVAL, "step_groups: null groups or work_list");
+  if ((int64_t)work_items * pl0.args.num_kv_heads > INT32_MAX)
+    return fail(PKV_EINVAL, "step_groups: work list too long");
+  DecodePlan pl = pl0;
+  DecodeArgs& a = pl.args;
+  a.cow_src = cow_src;
+  a.groups = groups;
+  a.num_groups = num_groups;
+  a.group_size = group_size;
+  a.group_heads = pl0.group;
+  a.work = reinterpret_cast<const uint32_t*>(work_list);
+  a.work_items = work_items;
+  return hip_status(launch_decode_partitions_groups(a, kv_dtype, head_dim, (int)rows,
+                                                    (hipStream_t)stream),
+                    "decode partitions (fork groups) launch");
+}
+
+int pkv_paged_attention_partitions_step_groups(
+    void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
+    const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+    float scale, int partition_size, const int32_t* groups, int num_groups, int group_size,
+    const int32_t* work_list, int work_items, void* workspace, size_t workspace_bytes,
+    int kv_policy, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  return groups_pass(pl, kv_dtype, head_dim, cow_src, groups, num_groups, group_size, work_list,
+                     work_items, stream);
+}
+
+int pkv_paged_attention_decode_step_groups(
+    void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
+    const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
+    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+    float scale, int partition_size, const int32_t* groups, int num_groups, int group_size,
+    const int32_t* work_list, int work_items, void* workspace, size_t workspace_bytes,
+    int kv_policy, void* stream) {
+  DecodePlan pl;
+  int st = plan_decode(&pl, out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, seq_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, kv_policy);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if ((st = append_args(&pl, k_new, v_new)) != PKV_OK) return st;
+  st = groups_pass(pl, kv_dtype, head_dim, cow_src, groups, num_groups, group_size, work_list,
+                   work_items, stream);
+  if (st != PKV_OK || pl.args.pmax <= 1) return st;
+  return hip_status(launch_decode_reduce(pl.args, head_dim, (hipStream_t)stream), "decode reduce launch");
 }
 
 static int prefix_pass(const DecodePlan& pl, int kv_dtype, int head_dim, int block_size,

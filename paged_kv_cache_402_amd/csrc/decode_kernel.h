@@ -172,8 +172,14 @@ __device__ __forceinline__ uint32_t timeline_now(const DecodeArgs& a) {
 // choice), else with the default one (batches whose sequences read the same blocks).
 // COW: the launch carries copy-on-write sources (cow_src); only those kernels hold the copy's
 // stores, so every other launch keeps the registers (and waves per SIMD) it had without them.
-template <int DT, int D, int G, bool MF, bool NTL, bool COW>
+// GRP: the work items name fork groups (DecodeArgs::groups) whose members attend to the same
+// tokens before their new ones: the group's G rows are several sequences' query heads, the
+// shared tokens are read once for all of them, and each row's own new token (its K and V rows
+// from k_new / v_new) is scored and added on its own. Launches with k_new and a work list only;
+// no matrix-core K pass.
+template <int DT, int D, int G, bool MF, bool NTL, bool COW, bool GRP = false>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(DecodeArgs a) {
+  static_assert(!(GRP && MF), "fork groups take the VALU K pass");
   using K = Cfg<DT, D, G>;
   auto load_kv = [](const unsigned char* p) -> u32x4 {
     if constexpr (NTL) return load16_stream(p);
@@ -214,18 +220,31 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
     b = (int)(w >> 16);
     pi = (int)(w & 0xFFFFu);
-    if (b >= a.num_seqs) return;
+    if (b >= (GRP ? a.num_groups : a.num_seqs)) return;
   } else {
     kvh = blockIdx.x;
     pi = blockIdx.y;
     b = blockIdx.z;
+  }
+  // fork group: the sequence of each row (-1: an empty place); its first member's table and
+  // length describe the tokens the rows share
+  int rowseq[G];
+  int lead = b;
+  if constexpr (GRP) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int m = a.groups[(size_t)b * a.group_size + g / a.group_heads];
+      rowseq[g] = (unsigned)m < (unsigned)a.num_seqs ? m : -1;
+    }
+    lead = rowseq[0];
+    if (lead < 0) return;
   }
   const int t0 = pi * a.part;                  // a multiple of the block size
   // ---- block ids of the partition (one per lane) and the query slices, issued together with
   // the length load: every table entry the partition could use (those past the sequence end
   // are never read again), so no load waits on another before the first K round ----
   const int32_t* __restrict__ trow =
-      a.block_tables + (size_t)b * a.max_blocks + (t0 >> a.bs_log2);
+      a.block_tables + (size_t)lead * a.max_blocks + (t0 >> a.bs_log2);
   const int pblk = min(a.part >> a.bs_log2, a.max_blocks - (t0 >> a.bs_log2));
   int ids[4];
 #pragma unroll
@@ -237,14 +256,23 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const int kc = lane % K::LK;  // this lane's vectors: kc, kc+LK, ...
   const unsigned char* qsrc =
       (const unsigned char*)a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * K::RB;
+  // query row of row g: head kvh * G + g of sequence b, or of a fork group's member
+  auto qrow = [&](int g) -> const unsigned char* {
+    if constexpr (GRP)
+      return (const unsigned char*)a.q +
+             ((size_t)max(rowseq[g], 0) * a.num_q_heads + (size_t)kvh * a.group_heads +
+              g % a.group_heads) * K::RB;
+    else
+      return qsrc + (size_t)g * K::RB;
+  };
   u32x4 qv[G][K::NLK];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int i = 0; i < K::NLK; ++i)
-      qv[g][i] = load16(qsrc + (size_t)(g * K::C + kc + i * K::LK) * 16);
+      qv[g][i] = load16(qrow(g) + (size_t)(kc + i * K::LK) * 16);
   const int cap = a.max_blocks << a.bs_log2;
-  int L = a.seq_lens[b];
+  int L = a.seq_lens[lead];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   const int nparts = L == 0 ? 1 : (L + a.part - 1) / a.part;
   if (pi >= nparts) return;
@@ -291,18 +319,70 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   // block when it uses it, so the copy costs stores only and no phase of its own. The new
   // token's row is written by the store below; rows past it hold no token of the sequence
   // and are left as they are (an append writes them before any read).
-  const int cow = (COW && fused && a.cow_src != nullptr && last >= 0 && last < n) ? a.cow_src[b] : -1;
+  const int cow = (COW && fused && a.cow_src != nullptr && last >= 0 && last < n) ? a.cow_src[lead] : -1;
   const int cow_dst =
       (unsigned)cow < (unsigned)a.num_blocks ? pick_id(ids, last >> a.bs_log2) : -1;
   const bool cow_live = (unsigned)cow < (unsigned)a.num_blocks && (unsigned)cow_dst < (unsigned)a.num_blocks;
-  const int cow_jb = cow_live ? last >> a.bs_log2 : -1;   // the last block, partition-relative
+  // fork group: every member that made a private copy of the new token's block gets the
+  // source rows stored into its copy (the member that kept the source, or members with a
+  // fresh block, have none); -1: no copy at that place
+  int gdst[G];
+  bool any_gdst = false;
+  if constexpr (GRP) {
+    const size_t jabs = (size_t)(t0 >> a.bs_log2) + (size_t)(max(last, 0) >> a.bs_log2);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      gdst[j] = -1;
+      if (COW && fused && a.cow_src != nullptr && last >= 0 && last < n && j < a.group_size) {
+        const int m = a.groups[(size_t)b * a.group_size + j];
+        if ((unsigned)m < (unsigned)a.num_seqs &&
+            (unsigned)a.cow_src[m] < (unsigned)a.num_blocks) {
+          const int dst = a.block_tables[(size_t)m * a.max_blocks + jabs];
+          gdst[j] = (unsigned)dst < (unsigned)a.num_blocks ? dst : -1;
+        }
+      }
+      any_gdst |= gdst[j] >= 0;
+    }
+  }
+  const int cow_jb = (GRP ? any_gdst : cow_live) ? last >> a.bs_log2 : -1;   // the last block, partition-relative
   // this KV head's tiles of the private copy (uniform; cow_live has checked the block id, and
   // every store below lands inside the tile: row < block_size, column < the row's bytes)
   unsigned char* const cow_k =
       const_cast<unsigned char*>(kbase) + (size_t)(cow_live ? cow_dst : 0) * block_bytes;
   unsigned char* const cow_v =
       const_cast<unsigned char*>(vbase) + (size_t)(cow_live ? cow_dst : 0) * block_bytes;
-  if (fused && last >= 0 && last < n && (packed || wave == 0)) {
+  // one 16-byte piece of a copied row (off: its byte offset in the tile) into the copy, or
+  // into every member's copy of a fork group
+  auto cow_put = [&](const unsigned char* base, unsigned char* one, size_t off, const u32x4& v) {
+    if constexpr (GRP) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (gdst[j] >= 0)
+          store16(const_cast<unsigned char*>(base) + (size_t)gdst[j] * block_bytes + off, v);
+    } else {
+      store16(one + off, v);
+    }
+  };
+  if (GRP && fused && last >= 0 && last < n && (packed || wave == 0)) {
+    // each member's new token into its own block (its table's entry for that position)
+    const size_t jabs = (size_t)(t0 >> a.bs_log2) + (size_t)(last >> a.bs_log2);
+    for (int j = 0; j < a.group_size; ++j) {
+      const int m = a.groups[(size_t)b * a.group_size + j];
+      if ((unsigned)m >= (unsigned)a.num_seqs) continue;
+      const int blk = a.block_tables[(size_t)m * a.max_blocks + jabs];
+      if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
+      const size_t row = (size_t)blk * block_bytes + (size_t)(last & bs_mask) * K::RB;
+      const size_t own = ((size_t)m * a.num_kv_heads + kvh) * K::RB;
+      for (int c = lane; c < 2 * K::C; c += 64) {
+        const bool isv = c >= K::C;
+        const int cc = isv ? c - K::C : c;
+        unsigned char* dst = (unsigned char*)(isv ? a.v_cache : a.k_cache) + kvh * head_bytes + row;
+        store16(dst + cc * 16,
+                load16((const unsigned char*)(isv ? a.v_new : a.k_new) + own + cc * 16));
+      }
+    }
+  }
+  if (!GRP && fused && last >= 0 && last < n && (packed || wave == 0)) {
     const int blk = pick_id(ids, last >> a.bs_log2);
     if ((unsigned)blk < (unsigned)a.num_blocks) {
       const size_t row = (size_t)blk * block_bytes + (size_t)(last & bs_mask) * K::RB;
@@ -411,7 +491,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         okb[u] = (unsigned)blk < (unsigned)a.num_blocks;
         const unsigned char* p = kbase + (size_t)(okb[u] ? blk : 0) * block_bytes +
                                  (uint32_t)(((tok & bs_mask) + kr) * K::RB + kc * 16);
-        if (fused && tok + kr == last) p = knew + kc * 16;
+        if (!GRP && fused && tok + kr == last) p = knew + kc * 16;
 #pragma unroll
         for (int i = 0; i < K::NLK; ++i) kv[u][i] = load_kv(p + i * K::LK * 16);
       } else {
@@ -428,7 +508,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         if (COW && (tok >> a.bs_log2) == cow_jb && tok + kr < last && tl < nw) {
 #pragma unroll
           for (int i = 0; i < K::NLK; ++i)
-            store16(cow_k + ((tok & bs_mask) + kr) * K::RB + (kc + i * K::LK) * 16, kv[u][i]);
+            cow_put(kbase, cow_k, (size_t)((tok & bs_mask) + kr) * K::RB + (kc + i * K::LK) * 16,
+                    kv[u][i]);
         }
         float s[G];
 #pragma unroll
@@ -438,7 +519,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
           for (int i = 0; i < K::NLK; ++i) acc = dot16<DT>(qv[g][i], kv[u][i], acc);
           s[g] = group_sum<K::LK>(acc) * a.scale_log2;
         }
-        const bool valid = okb[u] && tl < nw;
+        // a fork group's rows each have their own new token: scored after the pass
+        const bool valid = okb[u] && tl < nw && !(GRP && tok + kr == last);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           s[g] = valid ? s[g] : -INFINITY;
@@ -446,6 +528,25 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         }
         if (kc == 0 && tl < nw) lds_store_n<G>(s_sc + tl * G, s);
       }
+    }
+  }
+  if constexpr (GRP) {
+    // each row's own new token: its score against the member's K row from k_new, into the
+    // slot of that position (the pass above left -inf there)
+    if (fused && last >= c0 && last < c0 + nw) {
+      float so[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const unsigned char* kn = (const unsigned char*)a.k_new +
+                                  ((size_t)max(rowseq[g], 0) * a.num_kv_heads + kvh) * K::RB;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < K::NLK; ++i)
+          acc = dot16<DT>(qv[g][i], load16(kn + (kc + i * K::LK) * 16), acc);
+        so[g] = rowseq[g] >= 0 ? group_sum<K::LK>(acc) * a.scale_log2 : -INFINITY;
+        m[g] = fmaxf(m[g], so[g]);
+      }
+      if (lane == 0) lds_store_n<G>(s_sc + (last - c0) * G, so);
     }
   }
   // the wave's max (every lane ends with it); -inf when the share has no readable token
@@ -472,7 +573,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         okv[u] = (unsigned)blk < (unsigned)a.num_blocks;
         const unsigned char* p = vbase + (size_t)(okv[u] ? blk : 0) * block_bytes +
                                  (uint32_t)(((tok & bs_mask) + vr) * K::RB + vc * 16);
-        if (fused && tok + vr == last) p = vnew + vc * 16;
+        if (!GRP && fused && tok + vr == last) p = vnew + vc * 16;
 #pragma unroll
         for (int i = 0; i < K::NLV; ++i) vv[u][i] = load_kv(p + i * K::LV * 16);
       }
@@ -518,10 +619,11 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       if (COW && gi < ngv && (tok >> a.bs_log2) == cow_jb && tok + vr < last && tl < nw) {
 #pragma unroll
         for (int i = 0; i < K::NLV; ++i)
-          store16(cow_v + ((tok & bs_mask) + vr) * K::RB + (vc + i * K::LV) * 16, vv[u][i]);
+          cow_put(vbase, cow_v, (size_t)((tok & bs_mask) + vr) * K::RB + (vc + i * K::LV) * 16,
+                  vv[u][i]);
       }
       // tokens past the sequence end may hold anything (even NaN): skip, never multiply by 0
-      if (gi < ngv && okv[u] && tl < nw) {
+      if (gi < ngv && okv[u] && tl < nw && !(GRP && tok + vr == last)) {
         float pg[G];
         lds_load_n<G>(s_sc + tl * G, pg);
 #pragma unroll
@@ -533,6 +635,29 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
 #pragma unroll
             for (int e = 0; e < K::PER16; ++e)
               acc[g][i * K::PER16 + e] = __builtin_fmaf(pg[g], f[e], acc[g][i * K::PER16 + e]);
+        }
+      }
+    }
+  }
+
+  if constexpr (GRP) {
+    // each row's own new token: its weight times the member's V row from v_new, once per
+    // column (the lanes of the first row group)
+    if (fused && last >= c0 && last < c0 + nw && vr == 0) {
+      float pg[G];
+      lds_load_n<G>(s_sc + (last - c0) * G, pg);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (rowseq[g] < 0) continue;
+        const unsigned char* vn = (const unsigned char*)a.v_new +
+                                  ((size_t)rowseq[g] * a.num_kv_heads + kvh) * K::RB;
+#pragma unroll
+        for (int i = 0; i < K::NLV; ++i) {
+          float f[K::PER16];
+          widen<DT>(load16(vn + (vc + i * K::LV) * 16), f);
+#pragma unroll
+          for (int e = 0; e < K::PER16; ++e)
+            acc[g][i * K::PER16 + e] = __builtin_fmaf(pg[g], f[e], acc[g][i * K::PER16 + e]);
         }
       }
     }
@@ -552,10 +677,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     if (vr == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        const int sq = GRP ? rowseq[g] : b;                 // the row's sequence
+        if (sq < 0) continue;
+        const int h = GRP ? kvh * a.group_heads + g % a.group_heads : kvh * G + g;
         const float f = m[g] == -INFINITY ? 0.f : 1.f;
         const float den = __builtin_fmaf(f, l[g], 0.f);
-        const int h = kvh * G + g;
-        const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + pi;
+        const size_t slot = ((size_t)sq * a.num_q_heads + h) * a.pmax + pi;
 #pragma unroll
         for (int i = 0; i < K::NLV; ++i)
 #pragma unroll
@@ -563,7 +690,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
             const int d = (i * K::LV + vc) * K::PER16 + e;
             const float num = __builtin_fmaf(f, acc[g][i * K::PER16 + e], 0.f);
             if (single)
-              store_out(a.out, ((size_t)b * a.num_q_heads + h) * D + d,
+              store_out(a.out, ((size_t)sq * a.num_q_heads + h) * D + d,
                         den > 0.f ? num / den : 0.f, a.out_dtype);
             else
               a.ws_acc[slot * D + d] = num;
@@ -612,12 +739,18 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       num = __builtin_fmaf(f, w_acc(w)[g * D + d], num);
       den = __builtin_fmaf(f, w_l(w)[g], den);
     }
-    const int h = kvh * G + g;
+    int sq = b;                                              // the row's sequence
+    if constexpr (GRP) {
+      const int mm = a.groups[(size_t)b * a.group_size + g / a.group_heads];
+      sq = (unsigned)mm < (unsigned)a.num_seqs ? mm : -1;
+    }
+    if (sq < 0) continue;
+    const int h = GRP ? kvh * a.group_heads + g % a.group_heads : kvh * G + g;
     if (single) {
       const float y = den > 0.f ? num / den : 0.f;
-      store_out(a.out, ((size_t)b * a.num_q_heads + h) * D + d, y, a.out_dtype);
+      store_out(a.out, ((size_t)sq * a.num_q_heads + h) * D + d, y, a.out_dtype);
     } else {
-      const size_t slot = ((size_t)b * a.num_q_heads + h) * a.pmax + pi;
+      const size_t slot = ((size_t)sq * a.num_q_heads + h) * a.pmax + pi;
       a.ws_acc[slot * D + d] = num;
       if (d == 0) {
         a.ws_ml[slot * 2] = M;  // -inf when the partition had no readable token
@@ -632,9 +765,9 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
 // LDS (occupancy query, cached per kernel, LDS size and device); 0 if unknown.
 int resident_groups(const void* kernel, size_t lds);
 
-template <int DT, int D, int G, bool MF, bool NTL, bool COW>
+template <int DT, int D, int G, bool MF, bool NTL, bool COW, bool GRP = false>
 static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
-  const auto kernel = paged_decode_partition_kernel<DT, D, G, MF, NTL, COW>;
+  const auto kernel = paged_decode_partition_kernel<DT, D, G, MF, NTL, COW, GRP>;
   if (a.work != nullptr) {
     const int units = a.num_kv_heads * a.work_items;
     // Only the last half machine-full of units (half as many as fit at once) is handed out
@@ -656,40 +789,42 @@ static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int DT, int D, int G, bool COW>
+template <int DT, int D, int G, bool COW, bool GRP = false>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
   // Matrix-core scores for 16-bit data at G = 8, when a 16-token step stays inside one block
   // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured
   // faster (the padded 16-row product does 4x the work there and the K pass is not the limit).
-  constexpr bool kMF = DT != F32 && G == 8;
+  // Fork groups take the VALU pass.
+  constexpr bool kMF = DT != F32 && G == 8 && !GRP;
   const bool mf = kMF && a.bs_log2 >= 4 && a.part % 64 == 0;
   if (a.kv_cached)
-    return mf ? launch_k<DT, D, G, kMF, false, COW>(a, lds, stream)
-              : launch_k<DT, D, G, false, false, COW>(a, lds, stream);
-  return mf ? launch_k<DT, D, G, kMF, true, COW>(a, lds, stream)
-            : launch_k<DT, D, G, false, true, COW>(a, lds, stream);
+    return mf ? launch_k<DT, D, G, kMF, false, COW, GRP>(a, lds, stream)
+              : launch_k<DT, D, G, false, false, COW, GRP>(a, lds, stream);
+  return mf ? launch_k<DT, D, G, kMF, true, COW, GRP>(a, lds, stream)
+            : launch_k<DT, D, G, false, true, COW, GRP>(a, lds, stream);
 }
 
-template <int DT, int D, bool COW>
+// group: the rows of a workgroup (query heads per KV head, times the members of a fork group)
+template <int DT, int D, bool COW, bool GRP = false>
 static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_t<DT, D, 1, COW>(a, stream);
-    case 2: return launch_t<DT, D, 2, COW>(a, stream);
-    case 4: return launch_t<DT, D, 4, COW>(a, stream);
+    case 1: return launch_t<DT, D, 1, COW, GRP>(a, stream);
+    case 2: return launch_t<DT, D, 2, COW, GRP>(a, stream);
+    case 4: return launch_t<DT, D, 4, COW, GRP>(a, stream);
     case 8:
-      if constexpr (D <= 128) return launch_t<DT, D, 8, COW>(a, stream);
+      if constexpr (D <= 128) return launch_t<DT, D, 8, COW, GRP>(a, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int DT, bool COW>
+template <int DT, bool COW, bool GRP = false>
 static hipError_t launch_d(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_g<DT, 64, COW>(a, group, stream);
-    case 128: return launch_g<DT, 128, COW>(a, group, stream);
-    case 256: return launch_g<DT, 256, COW>(a, group, stream);
+    case 64: return launch_g<DT, 64, COW, GRP>(a, group, stream);
+    case 128: return launch_g<DT, 128, COW, GRP>(a, group, stream);
+    case 256: return launch_g<DT, 256, COW, GRP>(a, group, stream);
     default: return hipErrorInvalidValue;
   }
 }

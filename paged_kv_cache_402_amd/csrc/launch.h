@@ -61,6 +61,14 @@ struct DecodeArgs {
   int sched_static;
   // KV read policy: 0 non-temporal loads (streaming), 1 default cache policy (PKV_KV_CACHED)
   int kv_cached;
+  // Fork groups (null: none): work items name groups instead of sequences. Group i lists
+  // group_size sequences at groups[i * group_size ..] (-1: an empty place) that attend to the
+  // same tokens before their new one: the same length, the same blocks before the new
+  // token's block, and the same block (the source of their copies) for its earlier rows. The
+  // group's G rows are query head kvh * group_heads + r % group_heads of member r /
+  // group_heads; the first member's table and length describe the shared tokens.
+  const int32_t* groups;
+  int num_groups, group_size, group_heads;
 };
 
 // Bytes of the workspace header that holds the scheduling word.
@@ -79,6 +87,10 @@ size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part);
 // dimension when a work list is given).
 hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_dim, int group,
                                     hipStream_t stream);
+// The same over fork groups (DecodeArgs::groups set; decode_groups.hip); rows = query heads
+// per KV head x group size.
+hipError_t launch_decode_partitions_groups(const DecodeArgs& a, int kv_dtype, int head_dim,
+                                           int rows, hipStream_t stream);
 // Launches the partition merge (grid: Hq x B); only multi-partition sequences do work.
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream);
 

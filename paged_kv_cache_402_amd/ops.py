@@ -373,6 +373,86 @@ def paged_attention_partitions_step(out, q, k_new, v_new, cow_src, k_cache, v_ca
     return ws
 
 
+def plan_fork_groups(block_tables, seq_lens, cow_src, block_size: int, num_blocks: int,
+                     group_size: int):
+    """Host planner of the fork-group step (pkv_decode_plan_fork_groups) from host tables
+    [B][W], lengths [B] and copy sources [B] (or None). Returns (groups int32 [n][group_size],
+    -1 filling short groups; group_lens int32 [n])."""
+    tab = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if tab.ndim != 2 or lens.shape != (tab.shape[0],):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    B, W = tab.shape
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    cs = None
+    if cow_src is not None:
+        cs = np.ascontiguousarray(np.asarray(cow_src, dtype=np.int32))
+        if cs.shape != (B,):
+            raise ValueError("cow_src must be [B]")
+    args = (tab.ctypes.data_as(P_i32), lens.ctypes.data_as(P_i32),
+            cs.ctypes.data_as(P_i32) if cs is not None else None, B, max(W, 1), block_size,
+            num_blocks, group_size)
+    n = check(lib.pkv_decode_plan_fork_groups(*args, None, None, 0), "decode_plan_fork_groups")
+    groups = np.empty((max(n, 1), group_size), dtype=np.int32)
+    glens = np.empty(max(n, 1), dtype=np.int32)
+    check(lib.pkv_decode_plan_fork_groups(*args, groups.ctypes.data_as(P_i32),
+                                          glens.ctypes.data_as(P_i32), n),
+          "decode_plan_fork_groups")
+    return groups[:n], glens[:n]
+
+
+def _groups_arg(groups):
+    _i32(groups, "groups")
+    if groups.dim() != 2:
+        raise ValueError("groups must be int32 [num_groups][group_size]")
+    return groups.data_ptr(), groups.shape[0], groups.shape[1]
+
+
+def paged_attention_decode_step_groups(out, q, k_new, v_new, cow_src, k_cache, v_cache,
+                                       block_tables, seq_lens, scale, groups, work_list,
+                                       partition_size=None, workspace=None, kv_policy: int = 0):
+    """paged_attention_decode_step over fork groups (groups: device int32
+    [num_groups][group_size] from plan_fork_groups; work_list: a list over the groups'
+    lengths, plain or (list, rows) packed; cow_src: int32 [B] or None). Returns `out`."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    partition_size = _resolve_partition(partition_size, B, Hq, Hkv, D, bs, W, work_list)
+    _append_args(k_new, v_new, k_cache, B)
+    cs = _cow_arg(cow_src, B) if cow_src is not None else None
+    gp, ng, gs = _groups_arg(groups)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_decode_step_groups(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, gp, ng, gs,
+        wl, wn, ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
+        "paged_attention_decode_step_groups")
+    return out
+
+
+def paged_attention_partitions_step_groups(out, q, k_new, v_new, cow_src, k_cache, v_cache,
+                                           block_tables, seq_lens, scale, groups, work_list,
+                                           partition_size: int = DEFAULT_PARTITION,
+                                           workspace=None, kv_policy: int = 0):
+    """First pass of paged_attention_decode_step_groups only. Returns the workspace for
+    paged_attention_reduce."""
+    B, Hq, D, NB, Hkv, bs, kdt, odt, W = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                      seq_lens)
+    _append_args(k_new, v_new, k_cache, B)
+    cs = _cow_arg(cow_src, B) if cow_src is not None else None
+    gp, ng, gs = _groups_arg(groups)
+    ws, wsb = _workspace(q, B, Hq, W, bs, D, partition_size, workspace)
+    wl, wn = _work(work_list)
+    check(lib.pkv_paged_attention_partitions_step_groups(
+        out.data_ptr(), odt, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), cs,
+        k_cache.data_ptr(), v_cache.data_ptr(), kdt, block_tables.data_ptr(),
+        seq_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, W, float(scale), partition_size, gp, ng, gs,
+        wl, wn, ws.data_ptr() if ws is not None else None, wsb, int(kv_policy), _stream(q)),
+        "paged_attention_partitions_step_groups")
+    return ws
+
+
 def paged_attention_prefix(out, q, k_cache, v_cache, block_tables, seq_lens, scale, members,
                            prefix_partitions: int, workspace,
                            partition_size: int = DEFAULT_PARTITION):

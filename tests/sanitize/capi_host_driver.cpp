@@ -46,6 +46,18 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int, int, int group, hi
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_decode_partitions_groups(const DecodeArgs& a, int, int head_dim, int rows,
+                                           hipStream_t) {
+  check_decode_args(a);
+  CHECK(a.groups != nullptr && a.num_groups > 0 && a.group_size >= 1);
+  CHECK(a.group_heads == a.num_q_heads / a.num_kv_heads);
+  CHECK(rows == a.group_size * a.group_heads);
+  CHECK(rows == 1 || rows == 2 || rows == 4 || rows == 8);
+  CHECK(rows < 8 || head_dim <= 128);
+  CHECK(a.work != nullptr && a.k_new != nullptr && a.v_new != nullptr);
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t) {
   CHECK(a.pmax > 1 && a.ws_ml != nullptr && a.ws_acc != nullptr);
   CHECK(head_dim == 64 || head_dim == 128 || head_dim == 256);
@@ -163,6 +175,30 @@ static void shared_plan(const Batch& t) {
                        part);
 }
 
+static void fork_groups(const Batch& t) {
+  std::vector<int32_t> cow((size_t)std::max(t.B, 1));
+  for (int b = 0; b < t.B; ++b) cow[b] = choose<int>({-1, -1, pick(0, t.NB + 2), -9});
+  const int size = choose<int>({1, 2, 3, 4, 8, 0});
+  const int32_t* cs = choose({cow.data(), (int32_t*)nullptr});
+  const int n = pkv_decode_plan_fork_groups(t.tables.data(), t.lens.data(), cs, t.B, t.W, t.bs,
+                                            t.NB, size, nullptr, nullptr, 0);
+  if (n < 0) return;
+  CHECK(n <= t.B && (t.B == 0 || n >= 1));
+  std::vector<int32_t> groups((size_t)std::max(n, 1) * size), glens((size_t)std::max(n, 1));
+  CHECK(pkv_decode_plan_fork_groups(t.tables.data(), t.lens.data(), cs, t.B, t.W, t.bs, t.NB,
+                                    size, groups.data(), glens.data(), n) == n);
+  std::vector<int> seen((size_t)std::max(t.B, 1), 0);
+  for (int g = 0; g < n; ++g)
+    for (int j = 0; j < size; ++j) {
+      const int m = groups[(size_t)g * size + j];
+      if (m >= 0) {
+        CHECK(m < t.B);
+        ++seen[m];
+      }
+    }
+  for (int b = 0; b < t.B; ++b) CHECK(seen[b] == 1);
+}
+
 static void decode_calls(const Batch& t) {
   const int kv = choose<int>({PKV_F32, PKV_F16, PKV_BF16, 7});
   const int out_dt = choose<int>({kv, PKV_F32, PKV_F16});
@@ -198,6 +234,13 @@ static void decode_calls(const Batch& t) {
                                          fake(4), kv, tabs, lens, B, hq, hkv, d, t.bs, t.NB, t.W,
                                          0.1f, p2, choose({wl, (const int32_t*)nullptr}),
                                          choose<int>({n, 0, -1}), ws, wsb, policy, nullptr);
+    CHECK(st <= 0);
+    st = pkv_paged_attention_decode_step_groups(
+        out, out_dt, fake(2), fake(10), fake(11), reinterpret_cast<const int32_t*>(fake(12)),
+        fake(3), fake(4), kv, tabs, lens, B, hq, hkv, d, t.bs, t.NB, t.W, 0.1f, p2,
+        choose({reinterpret_cast<const int32_t*>(fake(14)), (const int32_t*)nullptr}),
+        pick(-1, B), choose<int>({1, 2, 4, 3, 0}), choose({wl, (const int32_t*)nullptr}),
+        choose<int>({n, 0, -1}), ws, wsb, policy, nullptr);
     CHECK(st <= 0);
     st = pkv_paged_attention_decode_shared(
         out, out_dt, fake(2), fake(3), fake(4), kv, tabs, lens, B, hq, hkv, d, t.bs, t.NB, t.W,
@@ -237,6 +280,7 @@ int main(int argc, char** argv) {
     const Batch t = random_batch();
     work_lists(t);
     shared_plan(t);
+    fork_groups(t);
     decode_calls(t);
     cache_calls(t);
     if (i % 97 == 0) {
