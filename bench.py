@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk",
-                   "llama13b_longtail", "llama3_8b_long_shared_prefix", "llama3_8b_short_batch",
+                   "llama13b_longtail", "llama13b_fork_long", "llama3_8b_long_shared_prefix",
+                   "llama3_8b_short_batch",
                    "tiny")
 
 
@@ -44,6 +45,12 @@ BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk
 # MI355X, cold steps): the long-tail mix 57.4 -> 53.1 us at 256 tokens (512: 62.9 us); the
 # short batch 124.7 -> 82.8 us at 48.
 DEFAULT_PACK = {"llama13b_longtail": 256, "llama3_8b_short_batch": 48}
+# parallel-sampling workloads (a fork per prompt, then one appended token per branch): their
+# generators in workloads/gen.py
+# grid of the workloads whose measured best is not the plain list
+DEFAULT_GRID = {"llama13b_fork_long": "forks"}
+FORKED = {"llama13b_longtail": "llama13b_longtail_case",
+          "llama13b_fork_long": "llama13b_fork_long_case"}
 
 
 def parse_args():
@@ -54,11 +61,15 @@ def parse_args():
     p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
     p.add_argument("--partition", type=int, default=0,
                    help="tokens per context partition (0: the library's default for the shapes)")
-    p.add_argument("--grid", choices=("shared", "list", "full"), default="list",
+    p.add_argument("--grid", choices=("shared", "list", "full", "forks"), default=None,
                    help="shared: partitions that a group of sequences shares run once for the "
                         "whole group on the matrix cores, the rest over a work list; list: "
                         "every partition over the host work list (one workgroup per partition "
-                        "that holds tokens); full: the full partition x sequence grid")
+                        "that holds tokens); full: the full partition x sequence grid; forks: "
+                        "the branches of each fork in one workgroup's rows, their shared tokens "
+                        "read once (workloads with a fused copy-on-write step). Default: "
+                        "the workload's measured best, %s, else list"
+                        % ", ".join("%s %s" % kv for kv in DEFAULT_GRID.items()))
     p.add_argument("--append", choices=("fused", "separate"), default="fused",
                    help="fused: the decode pass stores the new tokens' K/V itself; separate: "
                         "reshape_and_cache runs first as its own launch")
@@ -112,12 +123,12 @@ def log(msg):
 # workload set-up through the block manager
 # ---------------------------------------------------------------------------------------------
 
-def build_forked_state(pk, gen, torch, dev):
+def build_forked_state(pk, gen, torch, dev, maker):
     """Parallel sampling step: every prompt is forked into its branches, then each branch
     appends one token; branches whose last prompt block is partial copy it first (the manager
     emits the copy-on-write pairs). The timed step replays that step: copy_blocks of the same
     pairs, cache write of the same slots, decode over the same tables."""
-    fc = gen.llama13b_longtail_case(values=False)
+    fc = maker(values=False)
     bs, nb = fc.block_size, fc.num_blocks
     bm = pk.BlockManager(nb, bs, fc.free_order)
     for g, L in enumerate(fc.decode_lens.tolist()):
@@ -135,8 +146,9 @@ def build_forked_state(pk, gen, torch, dev):
 
 
 def build_state(name, pk, gen, torch, dev):
-    if name == "llama13b_longtail":
-        case, bm, slots, pairs, cow_src = build_forked_state(pk, gen, torch, dev)
+    if name in FORKED:
+        case, bm, slots, pairs, cow_src = build_forked_state(pk, gen, torch, dev,
+                                                             getattr(gen, FORKED[name]))
         B = case.num_seqs
         shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
         seed = 402100
@@ -791,6 +803,8 @@ def main():
 
     if args.pack < 0:
         args.pack = DEFAULT_PACK.get(args.workload, 0)
+    if args.grid is None:
+        args.grid = DEFAULT_GRID.get(args.workload, "list")
     log("setting up %s" % args.workload)
     st = build_state(args.workload, pk, gen, torch, dev)
     case = st["case"]
@@ -799,7 +813,36 @@ def main():
                                                   case.block_size, case.table_width)
     bytes_ = byte_model(case, part)
     work, members, pp, items = None, None, 0, None
-    if args.grid == "list" and args.pack > 0:
+    groups = None
+    if args.grid == "forks":
+        if "cow_src_host" not in st or args.append != "fused":
+            raise SystemExit("--grid forks needs a forked workload (%s) and the "
+                             % ", ".join(FORKED) +
+                             "fused append")
+        # as many branches per group as the rows of a workgroup allow (8 query rows at most)
+        gsize = max(1, min(case.meta.get("branches", 1),
+                           8 // (case.num_q_heads // case.num_kv_heads)))
+        groups_h, glens = pk.plan_fork_groups(case.block_tables, case.seq_lens,
+                                              st["cow_src_host"], case.block_size,
+                                              case.num_blocks, gsize)
+        groups = torch.from_numpy(np.ascontiguousarray(groups_h)).to(dev)
+        if args.pack > 0:
+            items, rows = pk.decode_work_list_packed(glens, case.table_width, case.block_size,
+                                                     part, args.pack)
+            work = (torch.from_numpy(items).to(dev), rows)
+        else:
+            items = pk.decode_work_list(glens, case.table_width, case.block_size, part)
+            work = torch.from_numpy(items).to(dev)
+        # table entries: each group's shared ones once, plus every member's entry of its new
+        # token's block; the group rows, the list and the groups' lengths
+        bs_ = case.block_size
+        per_seq_tables = 4 * int((-(-case.seq_lens.astype(np.int64) // bs_)).sum())
+        group_tables = 4 * int((-(-glens.astype(np.int64) // bs_)).sum()) + 4 * case.num_seqs
+        bytes_["decode_kernel"] += (group_tables - per_seq_tables + 4 * int(items.shape[0])
+                                    + 4 * groups_h.size - 4 * (case.num_seqs - groups_h.shape[0]))
+        log("fork groups: %d of up to %d sequences, work list %d entries"
+            % (groups_h.shape[0], gsize, items.shape[0]))
+    elif args.grid == "list" and args.pack > 0:
         items, rows = pk.decode_work_list_packed(case.seq_lens, case.table_width,
                                                  case.block_size, part, args.pack)
         work = (torch.from_numpy(items).to(dev), rows)
@@ -833,7 +876,11 @@ def main():
     # that pass reads (pkv_decode_kv_policy; the shared-prefix list leaves the shared
     # partitions to the prefix pass)
     policy = {"stream": pk.KV_STREAM, "cached": pk.KV_CACHED}.get(args.kv_policy)
-    if policy is None:
+    if policy is None and groups is not None:
+        # the list names groups: their first members' tables and the groups' lengths
+        policy = pk.decode_kv_policy(case.block_tables[groups_h[:, 0]], glens, case.block_size,
+                                     case.num_blocks, work_list=items, partition_size=part)
+    elif policy is None:
         policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, case.block_size,
                                      case.num_blocks, work_list=items, partition_size=part)
     log("KV read policy: %s" % ("cached" if policy == pk.KV_CACHED else "stream"))
@@ -879,6 +926,12 @@ def main():
         elif name == "shared_prefix":
             pk.paged_attention_prefix(st["out"], st["q"], st["k"], st["v"], st["tables"], st["lens"],
                                       case.scale, members, pp, ws, partition_size=part)
+        elif name == "decode_partitions" and groups is not None:
+            pk.paged_attention_partitions_step_groups(st["out"], st["q"], st["k_new"], st["v_new"],
+                                                      st["cow_src"], st["k"], st["v"],
+                                                      st["tables"], st["lens"], case.scale,
+                                                      groups, work, partition_size=part,
+                                                      workspace=ws, kv_policy=policy)
         elif name == "decode_partitions" and fused_cow:
             pk.paged_attention_partitions_step(st["out"], st["q"], st["k_new"], st["v_new"],
                                                st["cow_src"], st["k"], st["v"], st["tables"],
@@ -999,13 +1052,15 @@ def main():
                    "kv_dtype": case.dtype, "accumulate": "f32", "partition_size": part,
                    "grid": args.grid, "late_units": "static" if args.no_sched else "ticketed",
                    "kv_policy": "cached" if policy == pk.KV_CACHED else "stream",
-                   "pack_tokens": args.pack if args.grid == "list" else 0,
+                   "pack_tokens": args.pack if args.grid in ("list", "forks") else 0,
                    "append": "fused" if fused else "separate",
                    "copy_on_write": ("fused" if fused_cow else "separate")
                    if st["pairs"] is not None else "none",
                    "prefix_tokens": case.meta.get("prefix_tokens", 0),
                    "mean_seq_len": round(float(case.seq_lens.mean()), 1),
                    "num_blocks": case.num_blocks, "parallelism": "single GPU",
+                   **({"fork_groups": int(groups.shape[0]), "fork_group_size": int(groups.shape[1])}
+                      if groups is not None else {}),
                    **({"named_partition_size": 512,
                        "partition_note": "the workload's definition names 512-token partitions; "
                                          "run with --partition 512 for that form (the default "

@@ -326,22 +326,24 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   // fork group: every member that made a private copy of the new token's block gets the
   // source rows stored into its copy (the member that kept the source, or members with a
   // fresh block, have none); -1: no copy at that place
-  int gdst[G];
+  // fork group, per row g: the block of its member's table that holds the new token (-1:
+  // none), and the same block as a copy destination when the member made a private copy of it
+  // (only on the first row of each member, so each copy is stored once); the loads of all rows
+  // are independent and issue together
+  int rblk[G], gdst[G];
   bool any_gdst = false;
   if constexpr (GRP) {
+    const bool here = fused && last >= 0 && last < n;
     const size_t jabs = (size_t)(t0 >> a.bs_log2) + (size_t)(max(last, 0) >> a.bs_log2);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      gdst[j] = -1;
-      if (COW && fused && a.cow_src != nullptr && last >= 0 && last < n && j < a.group_size) {
-        const int m = a.groups[(size_t)b * a.group_size + j];
-        if ((unsigned)m < (unsigned)a.num_seqs &&
-            (unsigned)a.cow_src[m] < (unsigned)a.num_blocks) {
-          const int dst = a.block_tables[(size_t)m * a.max_blocks + jabs];
-          gdst[j] = (unsigned)dst < (unsigned)a.num_blocks ? dst : -1;
-        }
-      }
-      any_gdst |= gdst[j] >= 0;
+    for (int g = 0; g < G; ++g) {
+      const int blk =
+          here && rowseq[g] >= 0 ? a.block_tables[(size_t)rowseq[g] * a.max_blocks + jabs] : -1;
+      rblk[g] = (unsigned)blk < (unsigned)a.num_blocks ? blk : -1;
+      const int src = COW && here && rowseq[g] >= 0 && g % a.group_heads == 0 &&
+                              a.cow_src != nullptr ? a.cow_src[rowseq[g]] : -1;
+      gdst[g] = (unsigned)src < (unsigned)a.num_blocks ? rblk[g] : -1;
+      any_gdst |= gdst[g] >= 0;
     }
   }
   const int cow_jb = (GRP ? any_gdst : cow_live) ? last >> a.bs_log2 : -1;   // the last block, partition-relative
@@ -363,25 +365,6 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       store16(one + off, v);
     }
   };
-  if (GRP && fused && last >= 0 && last < n && (packed || wave == 0)) {
-    // each member's new token into its own block (its table's entry for that position)
-    const size_t jabs = (size_t)(t0 >> a.bs_log2) + (size_t)(last >> a.bs_log2);
-    for (int j = 0; j < a.group_size; ++j) {
-      const int m = a.groups[(size_t)b * a.group_size + j];
-      if ((unsigned)m >= (unsigned)a.num_seqs) continue;
-      const int blk = a.block_tables[(size_t)m * a.max_blocks + jabs];
-      if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
-      const size_t row = (size_t)blk * block_bytes + (size_t)(last & bs_mask) * K::RB;
-      const size_t own = ((size_t)m * a.num_kv_heads + kvh) * K::RB;
-      for (int c = lane; c < 2 * K::C; c += 64) {
-        const bool isv = c >= K::C;
-        const int cc = isv ? c - K::C : c;
-        unsigned char* dst = (unsigned char*)(isv ? a.v_cache : a.k_cache) + kvh * head_bytes + row;
-        store16(dst + cc * 16,
-                load16((const unsigned char*)(isv ? a.v_new : a.k_new) + own + cc * 16));
-      }
-    }
-  }
   if (!GRP && fused && last >= 0 && last < n && (packed || wave == 0)) {
     const int blk = pick_id(ids, last >> a.bs_log2);
     if ((unsigned)blk < (unsigned)a.num_blocks) {
@@ -539,10 +522,19 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       for (int g = 0; g < G; ++g) {
         const unsigned char* kn = (const unsigned char*)a.k_new +
                                   ((size_t)max(rowseq[g], 0) * a.num_kv_heads + kvh) * K::RB;
+        // the member's new K row also goes into its cache slot (once per member: its first
+        // row, by the lanes of the first token row)
+        unsigned char* slot = (unsigned char*)a.k_cache + kvh * head_bytes +
+                              (size_t)max(rblk[g], 0) * block_bytes +
+                              (size_t)(last & bs_mask) * K::RB;
+        const bool put = kr == 0 && rblk[g] >= 0 && g % a.group_heads == 0;
         float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < K::NLK; ++i)
-          acc = dot16<DT>(qv[g][i], load16(kn + (kc + i * K::LK) * 16), acc);
+        for (int i = 0; i < K::NLK; ++i) {
+          const u32x4 kx = load16(kn + (kc + i * K::LK) * 16);
+          if (put) store16(slot + (kc + i * K::LK) * 16, kx);
+          acc = dot16<DT>(qv[g][i], kx, acc);
+        }
         so[g] = rowseq[g] >= 0 ? group_sum<K::LK>(acc) * a.scale_log2 : -INFINITY;
         m[g] = fmaxf(m[g], so[g]);
       }
@@ -651,10 +643,17 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
         if (rowseq[g] < 0) continue;
         const unsigned char* vn = (const unsigned char*)a.v_new +
                                   ((size_t)rowseq[g] * a.num_kv_heads + kvh) * K::RB;
+        // the member's new V row also goes into its cache slot (once per member)
+        unsigned char* slot = (unsigned char*)a.v_cache + kvh * head_bytes +
+                              (size_t)max(rblk[g], 0) * block_bytes +
+                              (size_t)(last & bs_mask) * K::RB;
+        const bool put = rblk[g] >= 0 && g % a.group_heads == 0;
 #pragma unroll
         for (int i = 0; i < K::NLV; ++i) {
+          const u32x4 vx = load16(vn + (vc + i * K::LV) * 16);
+          if (put) store16(slot + (vc + i * K::LV) * 16, vx);
           float f[K::PER16];
-          widen<DT>(load16(vn + (vc + i * K::LV) * 16), f);
+          widen<DT>(vx, f);
 #pragma unroll
           for (int e = 0; e < K::PER16; ++e)
             acc[g][i * K::PER16 + e] = __builtin_fmaf(pg[g], f[e], acc[g][i * K::PER16 + e]);

@@ -338,6 +338,15 @@ def llama13b_longtail_case(groups: int = 32, branches: int = 4, values: bool = T
                               scale=float(np.float32(1.0 / math.sqrt(d))))
 
 
+def llama13b_fork_long_case(values: bool = True) -> ForkedSamplingCase:
+    """The long-tail shape (32 prompts x 4 branches, 40 MHA heads, head_dim 128, block 32, fp16)
+    over long prompts: decode lengths geometric with mean 2000, clipped to [1, 8192] (parallel
+    sampling over a document-length prompt, where the shared prompt dominates the bytes)."""
+    c = llama13b_longtail_case(values=values, mean_len=2000, max_len=8192)
+    c.name = "llama13b_fork_long_32x4_f16"
+    return c
+
+
 def long_context_splitk_case(num_seqs: int = 16, values: bool = True, poison: bool = True,
                              min_len: int = 32768, max_len: int = 131072) -> PagedDecodeCase:
     """Batch 16, 64 query / 8 KV heads, head_dim 128, block 64, bf16; seq_lens uniform on
