@@ -358,6 +358,7 @@ def cpu_baseline(st, target_s, gen):
 KERNEL_SOURCES = ("paged_kv_cache_402_amd/csrc/decode.hip",
                   "paged_kv_cache_402_amd/csrc/decode_kernel.h",
                   "paged_kv_cache_402_amd/csrc/decode_step.hip",
+                  "paged_kv_cache_402_amd/csrc/decode_groups.hip",
                   "paged_kv_cache_402_amd/csrc/common.h",
                   "paged_kv_cache_402_amd/csrc/launch.h")
 
