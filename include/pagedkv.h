@@ -366,7 +366,10 @@ int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_
  * cache row a sequence holds, are those of pkv_paged_attention_decode_step on the same
  * arguments: the cache rows bitwise, the outputs up to fp32 rounding order (the own token is
  * added after the shared ones). Sequences in no group get no output. num_seqs and num_groups
- * are at most 32767. */
+ * are at most 32767. A group's workgroup does the arithmetic of all its rows at the occupancy
+ * of a kernel with that many rows: it pays where the shared tokens dominate the bytes (forks
+ * of prompts of thousands of tokens: 1.5x faster measured), not for short prompts, whose
+ * per-sequence step is bound by load latency rather than bytes (there it measured slower). */
 int pkv_paged_attention_decode_step_groups(
     void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
     const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
