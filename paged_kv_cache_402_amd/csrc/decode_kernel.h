@@ -45,10 +45,6 @@
 //     v_new and are stored into the cache slot; and a copy-on-write of the last block is
 //     made by storing the source rows the passes read into the private copy as they are
 //     used (only in the kernels built for launches with copy sources, decode_step.hip);
-//   * fork groups (the GRP build): the G rows may be several sequences' query heads when
-//     those sequences attend to the same tokens before their new one (the branches of a fork
-//     right after it, P2 §2.2); the shared tokens are then read once for all of them, and each
-//     row's own new token is scored and added by itself after each pass;
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
 //     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence
 //     that fits one partition gets its output row directly, longer ones leave (max, sum,
