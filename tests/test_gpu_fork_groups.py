@@ -72,6 +72,8 @@ def _work(P, glens, W, bs, part, form):
     ("f32", 8, 4, 8, 64, "list", 4),          # 2 heads x 4 members, many partitions
     ("bf16", 16, 16, 16, 256, "packed", 8),   # MHA, 8 members (groups of 4 padded)
     ("f16", 32, 8, 16, 512, "list", 1),       # one member: the per-sequence rows
+    ("bf16", 64, 8, 64, 1024, "list", 1),     # 8 query heads per KV head, one member
+    ("f32", 16, 8, 16, 256, "packed", 2),     # head_dim 256 (f32 rows of 1 KiB), 2 x 2 rows
 ])
 def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form, group):
     """Prompts of many lengths (a partial last block, a full one, empty, longer than a
@@ -80,8 +82,8 @@ def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form
     outputs within fp32 rounding of it and within the gate of the oracle. Unwritten slots hold
     NaN, so a read of a row before it is written would show."""
     P = pk()
-    rng = np.random.default_rng(90 + group)
-    d = 128 if dtype != "f32" else 64
+    rng = np.random.default_rng(90 + group + hq)
+    d = 128 if dtype != "f32" else (256 if hq == 16 else 64)
     prompts = [3 * bs - 3, 2 * bs, part + 5, 1, 0, bs + 1, 2 * part - 1, 7]
     branches = [4, 3, 2, 1, 2, 4, 3, 1]
     nb, kd, vd, seqs, slots, pairs, cow_src, tables, lens, W = _forked_batch(
@@ -119,6 +121,47 @@ def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form
                               q=to_host(q, dtype), k_cache=to_host(k2, dtype),
                               v_cache=to_host(v2, dtype))
     assert max_err(o2.cpu().numpy().astype(np.float64), oracle(ref)) <= GATE[dtype]
+
+
+def test_out_of_pool_shared_entries_are_left_out_for_every_member():
+    """A table entry outside the pool in a fork's shared blocks (every member lists it, as forks
+    share their entries): the group step leaves that block's tokens out for all members, as the
+    per-sequence step does for each."""
+    P = pk()
+    rng = np.random.default_rng(97)
+    dtype, hq, hkv, bs, d, part = "f16", 8, 8, 16, 128, 256
+    nb, kd, vd, seqs, slots, pairs, cow_src, tables, lens, W = _forked_batch(
+        P, rng, dtype, hkv, d, bs, [5 * bs + 3, 3 * bs + 7], [4, 3])
+    B = len(seqs)
+    for b in range(4):
+        tables[b, 1] = -1                 # the first fork's second block, in every member
+    for b in range(4, B):
+        tables[b, 0] = nb + 3             # the second fork's first block, past the pool
+    groups, glens = P.plan_fork_groups(tables, lens, cow_src, bs, nb, 4)
+    assert groups.shape[0] == 2
+    q = to_dev(gen.normal(rng, (B, hq, d), dtype), dtype)
+    k_new = to_dev(gen.normal(rng, (B, hkv, d), dtype), dtype)
+    v_new = to_dev(gen.normal(rng, (B, hkv, d), dtype), dtype)
+    outs, caches = [], []
+    for grouped in (False, True):
+        k2, v2 = kd.clone(), vd.clone()
+        o = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        if grouped:
+            P.paged_attention_decode_step_groups(o, q, k_new, v_new, i32(cow_src), k2, v2,
+                                                 i32(tables), i32(lens), 0.09, i32(groups),
+                                                 i32(P.decode_work_list(glens, W, bs, part)),
+                                                 partition_size=part)
+        else:
+            P.paged_attention_decode_step(o, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
+                                          i32(lens), 0.09, partition_size=part,
+                                          work_list=i32(P.decode_work_list(lens, W, bs, part)))
+        torch.cuda.synchronize()
+        outs.append(o)
+        caches.append((k2, v2))
+    assert not torch.isnan(outs[1]).any()
+    assert torch.allclose(outs[0], outs[1], rtol=1e-5, atol=1e-6)
+    assert torch.equal(caches[0][0].view(torch.uint8), caches[1][0].view(torch.uint8))
+    assert torch.equal(caches[0][1].view(torch.uint8), caches[1][1].view(torch.uint8))
 
 
 def test_sequences_outside_every_group_are_left_alone():
