@@ -365,7 +365,10 @@ int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_
  * member whose cow_src names a source (cow_src may be NULL: no copies). Outputs, and every
  * cache row a sequence holds, are those of pkv_paged_attention_decode_step on the same
  * arguments: the cache rows bitwise, the outputs up to fp32 rounding order (the own token is
- * added after the shared ones). Sequences in no group get no output. num_seqs and num_groups
+ * added after the shared ones). The per-partition pass writes nothing for sequences in no
+ * group, but the merge that decode_step_groups runs afterwards covers every sequence longer
+ * than one partition: list every such sequence in a group (the planner's groups hold every
+ * sequence). num_seqs and num_groups
  * are at most 32767. A group's workgroup does the arithmetic of all its rows at the occupancy
  * of a kernel with that many rows: it pays where the shared tokens dominate the bytes (forks
  * of prompts of thousands of tokens: 1.5x faster measured), not for short prompts, whose

@@ -165,9 +165,10 @@ def test_out_of_pool_shared_entries_are_left_out_for_every_member():
 
 
 def test_sequences_outside_every_group_are_left_alone():
-    """A group list naming only some sequences: their rows and the caches they hold are
-    written, the other sequences' outputs are not, and the padded places of a short group
-    (-1, or a sequence index past the batch) are skipped."""
+    """A group list naming only some sequences (all of one partition, so the merge has nothing
+    to do for the others): the listed sequences' rows and the caches they hold are written, the
+    other sequences' outputs are not, and the padded places of a short group (-1, or a sequence
+    index past the batch) are skipped."""
     P = pk()
     rng = np.random.default_rng(95)
     dtype, hq, hkv, bs, d, part = "bf16", 8, 8, 16, 128, 256
