@@ -368,11 +368,11 @@ int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_
  * added after the shared ones). The per-partition pass writes nothing for sequences in no
  * group, but the merge that decode_step_groups runs afterwards covers every sequence longer
  * than one partition: list every such sequence in a group (the planner's groups hold every
- * sequence). num_seqs and num_groups
- * are at most 32767. A group's workgroup does the arithmetic of all its rows at the occupancy
- * of a kernel with that many rows: it pays where the shared tokens dominate the bytes (forks
- * of prompts of thousands of tokens: 1.5x faster measured), not for short prompts, whose
- * per-sequence step is bound by load latency rather than bytes (there it measured slower). */
+ * sequence). num_seqs and num_groups are at most 32767. A group's workgroup does the
+ * arithmetic of all its rows at the occupancy of a kernel with that many rows: it pays where
+ * the shared tokens dominate the bytes (forks of prompts of thousands of tokens: 1.5x faster
+ * measured), not for short prompts, whose per-sequence step is bound by load latency rather
+ * than bytes (there it measured slower). */
 int pkv_paged_attention_decode_step_groups(
     void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
     const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
