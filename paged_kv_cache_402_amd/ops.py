@@ -390,7 +390,7 @@ def plan_fork_groups(block_tables, seq_lens, cow_src, block_size: int, num_block
         if cs.shape != (B,):
             raise ValueError("cow_src must be [B]")
     args = (tab.ctypes.data_as(P_i32), lens.ctypes.data_as(P_i32),
-            cs.ctypes.data_as(P_i32) if cs is not None else None, B, max(W, 1), block_size,
+            cs.ctypes.data_as(P_i32) if cs is not None else None, B, W, block_size,
             num_blocks, group_size)
     n = check(lib.pkv_decode_plan_fork_groups(*args, None, None, 0), "decode_plan_fork_groups")
     groups = np.empty((max(n, 1), group_size), dtype=np.int32)
