@@ -45,6 +45,10 @@
 //     v_new and are stored into the cache slot; and a copy-on-write of the last block is
 //     made by storing the source rows the passes read into the private copy as they are
 //     used (only in the kernels built for launches with copy sources, decode_step.hip);
+//   * fork groups (the GRP build): the G rows may be several sequences' query heads when
+//     those sequences attend to the same tokens before their new one (the branches of a fork
+//     right after it, P2 §2.2); the shared tokens are then read once for all of them, and each
+//     row's own new token is scored and added by itself after each pass;
 //   * the lane rows of a wave are summed with shuffles, then the 4 waves are merged through
 //     LDS (each wave's data in its own, now dead, score area) with their maxima; a sequence
 //     that fits one partition gets its output row directly, longer ones leave (max, sum,
@@ -323,9 +327,6 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   const int cow_dst =
       (unsigned)cow < (unsigned)a.num_blocks ? pick_id(ids, last >> a.bs_log2) : -1;
   const bool cow_live = (unsigned)cow < (unsigned)a.num_blocks && (unsigned)cow_dst < (unsigned)a.num_blocks;
-  // fork group: every member that made a private copy of the new token's block gets the
-  // source rows stored into its copy (the member that kept the source, or members with a
-  // fresh block, have none); -1: no copy at that place
   // fork group, per row g: the block of its member's table that holds the new token (-1:
   // none), and the same block as a copy destination when the member made a private copy of it
   // (only on the first row of each member, so each copy is stored once); the loads of all rows
