@@ -372,7 +372,9 @@ int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_
  * arithmetic of all its rows at the occupancy of a kernel with that many rows: it pays where
  * the shared tokens dominate the bytes (forks of prompts of thousands of tokens: 1.5x faster
  * measured), not for short prompts, whose per-sequence step is bound by load latency rather
- * than bytes (there it measured slower). */
+ * than bytes (there it measured slower). kv_policy as for the other entry points; to pick it
+ * with pkv_decode_kv_policy, pass the groups' first members' table rows, the groups' lengths
+ * and the list over the groups (the reads the launch makes). */
 int pkv_paged_attention_decode_step_groups(
     void* out, int out_dtype, const void* q, const void* k_new, const void* v_new,
     const int32_t* cow_src, void* k_cache, void* v_cache, int kv_dtype,
