@@ -246,3 +246,51 @@ def test_group_step_long_tail_parallel_sampling():
     sub = gen.PagedDecodeCase("groups_sample", "f16", H, H, d, bs, nb, lens[pick], tables[pick],
                               c.scale, q=qh[pick], k_cache=kh, v_cache=vh)
     assert max_err(o2[pick].cpu().numpy().astype(np.float64), oracle(sub)) <= GATE["f16"]
+
+
+def test_group_step_long_prompt_forks_full_size():
+    """The long-prompt fork workload at full size (32 prompts x 4 branches of mean 1432 tokens,
+    40 MHA heads, fp16, block 32) in the launch the bench times (the groups' plain list,
+    2048-token partitions, the merge): caches bitwise those of the per-sequence step, outputs
+    within fp32 rounding of it, sampled sequences against the oracle."""
+    P = pk()
+    c = gen.llama13b_fork_long_case(values=False)
+    nb, bs, H, d, B = c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim, c.num_seqs
+    bm = P.BlockManager(nb, bs, c.free_order)
+    for g, L in enumerate(c.decode_lens.tolist()):
+        bm.add_seq(g * c.branches, L - 1)
+        for br in range(1, c.branches):
+            bm.fork(g * c.branches, g * c.branches + br)
+    slots, pairs, cow_src = bm.append_step(range(B))
+    tables, lens = bm.build_tables(range(B), c.table_width)
+    groups, glens = P.plan_fork_groups(tables, lens, cow_src, bs, nb, c.branches)
+    assert groups.shape == (len(c.decode_lens), c.branches)
+    shape = (nb, H, bs, d)
+    kd, vd = gen.device_normal(shape, "f16", 91, "cuda"), gen.device_normal(shape, "f16", 92, "cuda")
+    q = gen.device_normal((B, H, d), "f16", 93, "cuda")
+    k_new, v_new = gen.device_normal((B, H, d), "f16", 94, "cuda"), gen.device_normal((B, H, d), "f16", 95, "cuda")
+    part = 2048
+    k1, v1 = kd.clone(), vd.clone()
+    o1 = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
+    P.paged_attention_decode_step(o1, q, k_new, v_new, i32(cow_src), k1, v1, i32(tables),
+                                  i32(lens), c.scale, partition_size=part,
+                                  work_list=i32(P.decode_work_list(lens, c.table_width, bs, part)))
+    k2, v2 = kd.clone(), vd.clone()
+    o2 = torch.empty_like(o1)
+    ws = torch.empty(P.decode_workspace_bytes(B, H, c.table_width, bs, d, part), dtype=torch.uint8,
+                     device="cuda")
+    P.decode_workspace_init(ws)          # the bench's ticketed late units
+    P.paged_attention_decode_step_groups(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
+                                         i32(lens), c.scale, i32(groups),
+                                         i32(P.decode_work_list(glens, c.table_width, bs, part)),
+                                         partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
+    # fp16 outputs: the two orders of summation may round to neighbouring halves
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-3
+    kh, vh, qh = to_host(k2, "f16"), to_host(v2, "f16"), to_host(q, "f16")
+    pick = [0, 1, int(np.argmax(lens)), int(np.argmin(lens)), B - 1]
+    sub = gen.PagedDecodeCase("fork_long_sample", "f16", H, H, d, bs, nb, lens[pick], tables[pick],
+                              c.scale, q=qh[pick], k_cache=kh, v_cache=vh)
+    assert max_err(o2[pick].float().cpu().numpy().astype(np.float64), oracle(sub)) <= GATE["f16"]
