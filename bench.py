@@ -47,8 +47,10 @@ BENCH_WORKLOADS = ("llama3_8b_gqa_prefix", "llama2_7b_mha", "long_context_splitk
 DEFAULT_PACK = {"llama13b_longtail": 256, "llama3_8b_short_batch": 48}
 # parallel-sampling workloads (a fork per prompt, then one appended token per branch): their
 # generators in workloads/gen.py
-# grid of the workloads whose measured best is not the plain list
-DEFAULT_GRID = {"llama13b_fork_long": "forks"}
+# grid of the workloads whose measured best is not the plain list (cold steps, one MI355X):
+# the branches of long forked prompts 293.9 -> 195.8 us in fork groups; a 4096-token document
+# shared by 256 sequences 413 -> 118.5 us with the shared-prefix pass
+DEFAULT_GRID = {"llama13b_fork_long": "forks", "llama3_8b_long_shared_prefix": "shared"}
 FORKED = {"llama13b_longtail": "llama13b_longtail_case",
           "llama13b_fork_long": "llama13b_fork_long_case"}
 
@@ -93,6 +95,10 @@ def parse_args():
     p.add_argument("--no-sched", action="store_true",
                    help="leave the workspace's scheduling word uninitialised: every workgroup of "
                         "a work-list launch keeps its static unit (for comparison)")
+    p.add_argument("--keep-tail", action="store_true",
+                   help="leave the work list's ticketed tail as built, shared items included "
+                        "(default: pkv_decode_work_list_private_tail moves them out; for "
+                        "comparison)")
     p.add_argument("--kv-policy", choices=("auto", "stream", "cached"), default="auto",
                    help="cache policy of the decode kernel's KV reads; auto: "
                         "pkv_decode_kv_policy on the workload's tables")
@@ -122,6 +128,21 @@ def log(msg):
 # ---------------------------------------------------------------------------------------------
 # workload set-up through the block manager
 # ---------------------------------------------------------------------------------------------
+
+def private_tail(pk, st, items, tables, lens, part, kind, group_size=1):
+    """The work list with the units its launch hands out by ticket (the last half machine-full)
+    made of items that read no block another item reads (pkv_decode_work_list_private_tail):
+    a ticketed unit may run on another XCD than its KV head's, where a shared prefix is not in
+    L2."""
+    case = st["case"]
+    tail = pk.decode_ticketed_items(st["k"].dtype, case.head_dim, case.num_q_heads,
+                                    case.num_kv_heads, case.block_size, part, items.shape[0],
+                                    kind, group_size)
+    out, moved = pk.decode_work_list_private_tail(items, tables, lens, case.block_size,
+                                                  case.num_blocks, part, tail)
+    log("ticketed tail: %d items, %d shared items moved out of it" % (tail, moved))
+    return out, moved
+
 
 def build_forked_state(pk, gen, torch, dev, maker):
     """Parallel sampling step: every prompt is forked into its branches, then each branch
@@ -372,25 +393,41 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch of the decode kernel from profiles/hbm_traffic_<workload>.txt:
+# the launch settings that a traffic profile must share with the run it is reported for
+TRAFFIC_LAUNCH_KEYS = ("partition_size", "grid", "pack_tokens", "append", "copy_on_write",
+                       "kv_policy", "late_units", "ticketed_tail_shared_items_moved")
+
+
+def traffic_launch_key(config):
+    return ",".join("%s=%s" % (k, config.get(k)) for k in TRAFFIC_LAUNCH_KEYS)
+
+
+def measured_traffic(workload_name, config):
+    """HBM bytes per launch of the decode kernel from profiles/hbm_traffic_<workload>*.txt:
     FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
-    copy of known size. None when no such file exists or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % workload_name)
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    try:
-        return int(float(kv["traffic_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+    copy of known size. Only a profile of the same launch settings counts (its launch_key);
+    None when there is none, or when the kernel sources changed since it was taken."""
+    key = traffic_launch_key(config)
+    prefix = "hbm_traffic_%s" % workload_name
+    pdir = os.path.join(ROOT, "profiles")
+    for fname in sorted(os.listdir(pdir)):
+        if not (fname.startswith(prefix) and fname.endswith(".txt")):
+            continue
+        kv = {}
+        with open(os.path.join(pdir, fname)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload_name or kv.get("launch_key") != key:
+            continue
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        try:
+            return int(float(kv["traffic_bytes_per_launch"]))
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def copy_probe(pk, torch, dev):
@@ -815,6 +852,14 @@ def main():
     bytes_ = byte_model(case, part)
     work, members, pp, items = None, None, 0, None
     groups = None
+    # no workspace: no sequence spans two partitions and the merge pass has nothing to do
+    ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
+                                         case.block_size, case.head_dim, part)
+    # the ticketed tail made private (late units are ticketed only over an initialised
+    # workspace)
+    reorder_tail = ws_bytes > 0 and not args.no_sched and not args.keep_tail
+    moved = 0
+    kind = "copy_on_write" if st["pairs"] is not None and args.append == "fused" else "plain"
     if args.grid == "forks":
         if "cow_src_host" not in st or args.append != "fused":
             raise SystemExit("--grid forks needs a forked workload (%s) and the "
@@ -833,6 +878,9 @@ def main():
             work = (torch.from_numpy(items).to(dev), rows)
         else:
             items = pk.decode_work_list(glens, case.table_width, case.block_size, part)
+            if reorder_tail:
+                items, moved = private_tail(pk, st, items, case.block_tables[groups_h[:, 0]],
+                                            glens, part, "fork_groups", gsize)
             work = torch.from_numpy(items).to(dev)
         # table entries: each group's shared ones once, plus every member's entry of its new
         # token's block; the group rows, the list and the groups' lengths
@@ -851,6 +899,9 @@ def main():
         log("work list: %d rows, %d entries" % (rows, items.shape[0]))
     elif args.grid == "list":
         items = pk.decode_work_list(case.seq_lens, case.table_width, case.block_size, part)
+        if reorder_tail:
+            items, moved = private_tail(pk, st, items, case.block_tables, case.seq_lens, part,
+                                        kind)
         work = torch.from_numpy(items).to(dev)
         bytes_["decode_kernel"] += 4 * int(items.shape[0])     # one item read per launch
     elif args.grid == "shared":
@@ -885,9 +936,6 @@ def main():
         policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, case.block_size,
                                      case.num_blocks, work_list=items, partition_size=part)
     log("KV read policy: %s" % ("cached" if policy == pk.KV_CACHED else "stream"))
-    # no workspace: no sequence spans two partitions and the merge pass has nothing to do
-    ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
-                                         case.block_size, case.head_dim, part)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     if ws_bytes and not args.no_sched:
         pk.decode_workspace_init(ws)     # list launches hand out late units from its header
@@ -1052,6 +1100,7 @@ def main():
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "kv_dtype": case.dtype, "accumulate": "f32", "partition_size": part,
                    "grid": args.grid, "late_units": "static" if args.no_sched else "ticketed",
+                   "ticketed_tail_shared_items_moved": moved,
                    "kv_policy": "cached" if policy == pk.KV_CACHED else "stream",
                    "pack_tokens": args.pack if args.grid in ("list", "forks") else 0,
                    "append": "fused" if fused else "separate",
@@ -1075,12 +1124,14 @@ def main():
         "kernel_ms": stage_ms,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(case.name),
+                     "traffic": None,
                      "kernel": "paged_decode_partition_kernel",
                      "scope": "the decode partition kernel alone, per launch; the whole "
                               "step's fraction is frac_of_hbm_peak",
                      "bytes_per_launch": kernel_bytes},
     }
+    result["roofline"]["traffic"] = measured_traffic(case.name, result["config"])
+    result["traffic_launch_key"] = traffic_launch_key(result["config"])
     if probe is not None:
         ach = probe_rate(probe, "stream_2GiB", "nontemporal")
         result["achievable_GBps"] = ach

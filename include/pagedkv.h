@@ -234,6 +234,44 @@ int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_b
                                 int block_size, int partition_size, int pack_tokens,
                                 int32_t* work_list, int capacity, int* rows);
 
+/* Kinds of per-partition launch, for pkv_decode_ticketed_items: the _list, _append, _shared
+ * and plain entry points (PKV_LAUNCH_PLAIN), those with copy-on-write sources, the _step
+ * entry points (PKV_LAUNCH_COPY_ON_WRITE), and the fork-group step (PKV_LAUNCH_FORK_GROUPS). */
+enum { PKV_LAUNCH_PLAIN = 0, PKV_LAUNCH_COPY_ON_WRITE = 1, PKV_LAUNCH_FORK_GROUPS = 2 };
+
+/* How many items at the end of a work list of list_len items a launch with an initialised
+ * workspace (pkv_decode_workspace_init) hands out by ticket on the current device: the units
+ * of its last workgroups, half as many as are resident at once (or those past the first
+ * machine-full when there are fewer), rounded up to whole items (an item is num_kv_heads
+ * units). The sizes and dtypes are the launch's; group_size is the
+ * fork groups' size for PKV_LAUNCH_FORK_GROUPS and ignored otherwise. Queries the occupancy
+ * of the kernel such a launch picks (no launch; PKV_EHIP without a usable device). Returns the
+ * count (0: nothing is ticketed, as when the list holds no more units than fit at once),
+ * negative on bad arguments. (A gfx950 scheduling matter; no page defines it.) */
+int pkv_decode_ticketed_items(int kv_dtype, int head_dim, int num_q_heads, int num_kv_heads,
+                              int block_size, int partition_size, int list_len, int launch_kind,
+                              int group_size);
+
+/* Reorders a host work list from pkv_decode_work_list (not a packed one) in place, so that the
+ * items a launch hands out by ticket read no block that another item of the list reads too.
+ * A ticketed unit runs on whichever XCD has room, where the blocks its sequence shares with
+ * others (a common prompt prefix, P1 §6.1; P3 §2.2.8) are not in that XCD's L2, and are read
+ * from HBM again; a unit that keeps its place keeps its KV head's XCD, where they are. An item
+ * is shared when one of the in-pool blocks its tokens read (lengths clamped as the kernel
+ * clamps them) is read by the list more than once. If any of the last tail_items items (from
+ * pkv_decode_ticketed_items) is shared, the list's last tail_items private items move to its
+ * end, keeping their order, and every other item keeps its order before them; the walk back
+ * for private items stops at the first one over 5/4 of the longest item of the old tail, so the
+ * end of the launch does not grow much longer (a long item placed last lengthens its drain by
+ * more than the re-reads save); when no private item from before the tail qualifies, the list
+ * stays as it is. Outputs are bitwise the same in any item order. Returns how many shared
+ * items left the tail (0: the list is unchanged), negative on bad arguments
+ * (items naming a sequence >= num_seqs or a packed row). O(reads + list_len) on the host. */
+int pkv_decode_work_list_private_tail(const int32_t* block_tables, const int32_t* seq_lens,
+                                      int num_seqs, int max_blocks_per_seq, int block_size,
+                                      int num_blocks, int partition_size, int tail_items,
+                                      int32_t* work_list, int list_len);
+
 /* pkv_paged_attention_decode / _partitions with the per-partition pass launched over a work
  * list (device int32, from pkv_decode_work_list, or pkv_decode_work_list_packed with
  * work_items its rows) instead of the full (partition, sequence) grid: one workgroup per

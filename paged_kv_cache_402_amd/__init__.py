@@ -12,7 +12,8 @@ from .block_manager import BlockManager  # noqa: F401
 from .scheduler import Scheduler  # noqa: F401
 from .pool_plan import kv_pool_plan  # noqa: F401
 from .ops import (KV_CACHED, KV_STREAM, copy_blocks, decode_kv_policy,  # noqa: F401
-                  decode_work_list, decode_work_list_packed,
+                  decode_ticketed_items, decode_work_list, decode_work_list_packed,
+                  decode_work_list_private_tail,
                   decode_workspace_bytes, decode_workspace_init,
                   default_partition,
                   paged_attention_decode, paged_attention_decode_append,

@@ -46,6 +46,10 @@ SIGNATURES = {
     "pkv_decode_work_list": (c_int, [P_i32, c_int, c_int, c_int, c_int, P_i32, c_int]),
     "pkv_decode_work_list_packed": (c_int, [P_i32, c_int, c_int, c_int, c_int, c_int, P_i32,
                                             c_int, P_int]),
+    "pkv_decode_ticketed_items": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                          c_int, c_int]),
+    "pkv_decode_work_list_private_tail": (c_int, [P_i32, P_i32, c_int, c_int, c_int, c_int,
+                                                  c_int, c_int, P_i32, c_int]),
     "pkv_paged_attention_decode_list": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                                 c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                                 c_int, c_int, c_int, c_int, c_float, c_int,

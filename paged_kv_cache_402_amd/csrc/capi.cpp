@@ -411,6 +411,162 @@ int pkv_decode_work_list_packed(const int32_t* seq_lens, int num_seqs, int max_b
   return st;
 }
 
+int pkv_decode_ticketed_items(int kv_dtype, int head_dim, int num_q_heads, int num_kv_heads,
+                              int block_size, int partition_size, int list_len, int launch_kind,
+                              int group_size) {
+  if (!dtype_ok(kv_dtype)) return fail(PKV_EDTYPE, "ticketed_items: unknown kv dtype %d", kv_dtype);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "ticketed_items: query heads must be a positive multiple of kv heads");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PKV_EINVAL, "ticketed_items: head_dim must be 64, 128 or 256");
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 256)
+    return fail(PKV_EINVAL, "ticketed_items: block_size must be a power of two in [8, 256]");
+  if (partition_size == 0) partition_size = 512;
+  if (partition_size < 32 || partition_size > 2048 || partition_size % 32 != 0 ||
+      partition_size % block_size != 0)
+    return fail(PKV_EINVAL, "ticketed_items: bad partition_size");
+  if (list_len < 0 || (int64_t)list_len * num_kv_heads > INT32_MAX)
+    return fail(PKV_EINVAL, "ticketed_items: list_len out of range");
+  if (launch_kind != PKV_LAUNCH_PLAIN && launch_kind != PKV_LAUNCH_COPY_ON_WRITE &&
+      launch_kind != PKV_LAUNCH_FORK_GROUPS)
+    return fail(PKV_EINVAL, "ticketed_items: unknown launch_kind %d", launch_kind);
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t rows =
+      launch_kind == PKV_LAUNCH_FORK_GROUPS ? (int64_t)std::max(group_size, 0) * group : group;
+  if (rows != 1 && rows != 2 && rows != 4 && rows != 8)
+    return fail(PKV_EINVAL, "ticketed_items: rows per workgroup must be 1, 2, 4 or 8 (got %lld)",
+                (long long)rows);
+  if (rows == 8 && head_dim > 128)
+    return fail(PKV_EINVAL, "ticketed_items: 8 rows need head_dim <= 128");
+  if ((head_dim * elem_bytes(kv_dtype)) % 128 != 0)
+    return fail(PKV_EINVAL, "ticketed_items: row bytes must be a multiple of 128");
+  if (decode_lds_bytes(kv_dtype, head_dim, (int)rows, partition_size) > kMaxDecodeLds)
+    return fail(PKV_EINVAL, "ticketed_items: partition_size too large for LDS at this group size");
+  if (list_len == 0) return ok();
+  // the kernel a launch with these arguments picks depends on the sizes, the dtypes and the
+  // kind of launch only (both KV read policies build to the same occupancy)
+  DecodeArgs a{};
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.bs_log2 = log2i(block_size);
+  a.part = partition_size;
+  a.work_items = list_len;
+  a.group_size = launch_kind == PKV_LAUNCH_FORK_GROUPS ? group_size : 1;
+  a.group_heads = group;
+  int ticketed = 0;
+  hipError_t e;
+  if (launch_kind == PKV_LAUNCH_FORK_GROUPS)
+    e = launch_decode_partitions_groups(a, kv_dtype, head_dim, (int)rows, nullptr, &ticketed);
+  else if (launch_kind == PKV_LAUNCH_COPY_ON_WRITE)
+    e = launch_decode_partitions_cow(a, kv_dtype, head_dim, group, nullptr, &ticketed);
+  else
+    e = launch_decode_partitions(a, kv_dtype, head_dim, group, nullptr, &ticketed);
+  const int st = hip_status(e, "ticketed_items: occupancy query");
+  if (st != PKV_OK) return st;
+  return (ticketed + num_kv_heads - 1) / num_kv_heads;
+}
+
+int pkv_decode_work_list_private_tail(const int32_t* block_tables, const int32_t* seq_lens,
+                                      int num_seqs, int max_blocks_per_seq, int block_size,
+                                      int num_blocks, int partition_size, int tail_items,
+                                      int32_t* work_list, int list_len) {
+  if (partition_size == 0) partition_size = 512;
+  int st = check_list_args("private_tail", num_seqs, max_blocks_per_seq, block_size,
+                           partition_size);
+  if (st != PKV_OK) return st;
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "private_tail: num_blocks must be positive");
+  if (tail_items < 0 || list_len < 0)
+    return fail(PKV_EINVAL, "private_tail: negative tail_items or list_len");
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "private_tail: null block_tables or seq_lens");
+  if (list_len > 0 && !work_list) return fail(PKV_EINVAL, "private_tail: null work_list");
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  for (int i = 0; i < list_len; ++i) {
+    const uint32_t w = (uint32_t)work_list[i];
+    if (w & kPackedRow) return fail(PKV_EINVAL, "private_tail: packed lists are not reordered");
+    if ((int)(w >> 16) >= num_seqs)
+      return fail(PKV_EINVAL, "private_tail: item %d names sequence %d of %d", i, (int)(w >> 16),
+                  num_seqs);
+  }
+  const int T = std::min(tail_items, list_len);
+  if (T == 0) return ok();
+  auto tokens = [&](uint32_t w) {   // tokens of the item's partition (0 past the end)
+    const int64_t L = std::min<int64_t>(std::max(seq_lens[w >> 16], 0), cap);
+    return std::max<int64_t>(0, std::min<int64_t>(partition_size,
+                                                  L - (int64_t)(w & 0xFFFFu) * partition_size));
+  };
+  // how many reads each block gets from the whole list (in-pool table entries of every item's
+  // tokens); per-thread stamps keep a call at O(reads) rather than a pass over the pool
+  thread_local std::vector<uint32_t> stamp, count;
+  thread_local uint32_t epoch = 0;
+  if (stamp.size() < (size_t)num_blocks) {
+    stamp.resize((size_t)num_blocks, 0);
+    count.resize((size_t)num_blocks, 0);
+  }
+  if (++epoch == 0) {
+    std::fill(stamp.begin(), stamp.end(), 0u);
+    epoch = 1;
+  }
+  auto for_blocks = [&](uint32_t w, auto&& f) {
+    const int64_t n = tokens(w);
+    if (n == 0) return;
+    const int64_t t0 = (int64_t)(w & 0xFFFFu) * partition_size;
+    const int32_t* row = block_tables + (size_t)(w >> 16) * max_blocks_per_seq;
+    for (int64_t j = t0 / block_size; j < (t0 + n + block_size - 1) / block_size; ++j)
+      if (row[j] >= 0 && row[j] < num_blocks) f(row[j]);
+  };
+  for (int i = 0; i < list_len; ++i)
+    for_blocks((uint32_t)work_list[i], [&](int32_t id) {
+      if (stamp[id] != epoch) {
+        stamp[id] = epoch;
+        count[id] = 0;
+      }
+      ++count[id];
+    });
+  std::vector<char> shared((size_t)list_len, 0);
+  for (int i = 0; i < list_len; ++i)
+    for_blocks((uint32_t)work_list[i], [&](int32_t id) {
+      if (count[id] > 1) shared[i] = 1;
+    });
+  int before = 0;
+  int64_t longest = 0;
+  for (int i = list_len - T; i < list_len; ++i) {
+    before += shared[i];
+    longest = std::max(longest, tokens((uint32_t)work_list[i]));
+  }
+  if (before == 0) return ok();
+  // the new tail: the last T private items of the list, walking back from its end and
+  // stopping at the first private item more than a quarter longer than the old tail's
+  // longest (a long item at the end of the launch would lengthen its drain by more than the
+  // re-read it saves)
+  const int64_t limit = longest + longest / 4;
+  std::vector<char> moved((size_t)list_len, 0);
+  int k = 0;
+  for (int i = list_len - 1; i >= 0 && k < T; --i) {
+    if (shared[i]) continue;
+    if (tokens((uint32_t)work_list[i]) > limit) break;
+    moved[i] = 1;
+    ++k;
+  }
+  if (k == T - before) return ok();   // no private item to spare: the list stays as it is
+  std::vector<int32_t> out;
+  out.reserve((size_t)list_len);
+  for (int i = 0; i < list_len; ++i)
+    if (!moved[i]) out.push_back(work_list[i]);
+  for (int i = 0; i < list_len; ++i)
+    if (moved[i]) out.push_back(work_list[i]);
+  std::copy(out.begin(), out.end(), work_list);
+  int after = 0;
+  for (int i = list_len - T; i < list_len; ++i) {
+    const uint32_t w = (uint32_t)out[i];
+    bool sh = false;
+    for_blocks(w, [&](int32_t id) { sh = sh || count[id] > 1; });
+    after += sh;
+  }
+  ok();
+  return before - after;
+}
+
 int pkv_decode_plan_fork_groups(const int32_t* block_tables, const int32_t* seq_lens,
                                 const int32_t* cow_src, int num_seqs, int max_blocks_per_seq,
                                 int block_size, int num_blocks, int group_size, int32_t* groups,

@@ -118,12 +118,13 @@ int resident_groups(const void* kernel, size_t lds) {
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_dim, int group,
-                                    hipStream_t stream) {
-  if (a.cow_src != nullptr) return launch_decode_partitions_cow(a, kv_dtype, head_dim, group, stream);
+                                    hipStream_t stream, int* ticketed) {
+  if (a.cow_src != nullptr)
+    return launch_decode_partitions_cow(a, kv_dtype, head_dim, group, stream, ticketed);
   switch (kv_dtype) {
-    case F32: return launch_d<F32, false>(a, head_dim, group, stream);
-    case F16: return launch_d<F16, false>(a, head_dim, group, stream);
-    case BF16: return launch_d<BF16, false>(a, head_dim, group, stream);
+    case F32: return launch_d<F32, false>(a, head_dim, group, stream, ticketed);
+    case F16: return launch_d<F16, false>(a, head_dim, group, stream, ticketed);
+    case BF16: return launch_d<BF16, false>(a, head_dim, group, stream, ticketed);
     default: return hipErrorInvalidValue;
   }
 }

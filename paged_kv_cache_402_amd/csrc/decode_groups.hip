@@ -8,11 +8,11 @@
 namespace pkv {
 
 hipError_t launch_decode_partitions_groups(const DecodeArgs& a, int kv_dtype, int head_dim,
-                                           int rows, hipStream_t stream) {
+                                           int rows, hipStream_t stream, int* ticketed) {
   switch (kv_dtype) {
-    case F32: return launch_d<F32, true, true>(a, head_dim, rows, stream);
-    case F16: return launch_d<F16, true, true>(a, head_dim, rows, stream);
-    case BF16: return launch_d<BF16, true, true>(a, head_dim, rows, stream);
+    case F32: return launch_d<F32, true, true>(a, head_dim, rows, stream, ticketed);
+    case F16: return launch_d<F16, true, true>(a, head_dim, rows, stream, ticketed);
+    case BF16: return launch_d<BF16, true, true>(a, head_dim, rows, stream, ticketed);
     default: return hipErrorInvalidValue;
   }
 }

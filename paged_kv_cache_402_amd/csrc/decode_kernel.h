@@ -765,21 +765,37 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
 // LDS (occupancy query, cached per kernel, LDS size and device); 0 if unknown.
 int resident_groups(const void* kernel, size_t lds);
 
+// The first unit of a work-list launch of `units` units that is handed out by ticket (units:
+// none), for a kernel of which `resident` workgroups fit on the device at once (0: unknown).
+// Only the last half machine-full of units (half as many as fit at once) is handed out by
+// ticket: the list runs longest first, so those are its shortest units, enough to even out
+// the XCDs' finishing times. Every earlier workgroup keeps its static unit, and with it the
+// XCD of its KV head: a unit moved to another XCD reads the blocks its sequences share (a
+// common prefix) from HBM again instead of that XCD's L2. With non-temporal KV loads,
+// ticketing a whole machine-full cost more in such re-reads than it saved.
+static inline int ticket_start(int units, int resident) {
+  const int late = resident / 2;
+  const int first = units - late > resident ? units - late : resident;
+  return late <= 0 || first >= units ? units : first;
+}
+
+// With `ticketed` non-null nothing is launched: *ticketed receives how many of the launch's
+// units would be handed out by ticket (an error if the occupancy query fails).
 template <int DT, int D, int G, bool MF, bool NTL, bool COW, bool GRP = false>
-static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
+static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream, int* ticketed) {
   const auto kernel = paged_decode_partition_kernel<DT, D, G, MF, NTL, COW, GRP>;
+  if (ticketed != nullptr) {
+    const int units = a.num_kv_heads * a.work_items;
+    const int resident = resident_groups((const void*)kernel, lds);
+    if (resident <= 0) return hipErrorNoDevice;
+    *ticketed = units - ticket_start(units, resident);
+    return hipSuccess;
+  }
   if (a.work != nullptr) {
     const int units = a.num_kv_heads * a.work_items;
-    // Only the last half machine-full of units (half as many as fit at once) is handed out
-    // by ticket: the list runs longest first, so those are its shortest units, enough to even
-    // out the XCDs' finishing times. Every earlier workgroup keeps its static unit, and with
-    // it the XCD of its KV head: a unit moved to another XCD reads the blocks its sequences
-    // share (a common prefix) from HBM again instead of that XCD's L2. With non-temporal KV
-    // loads, ticketing a whole machine-full cost more in such re-reads than it saved.
     const int resident = a.sched != nullptr ? resident_groups((const void*)kernel, lds) : 0;
-    const int late = resident / 2;
-    a.sched_static = units - late > resident ? units - late : resident;
-    if (late <= 0 || a.sched_static >= units) a.sched = nullptr;
+    a.sched_static = ticket_start(units, resident);
+    if (a.sched_static >= units) a.sched = nullptr;
     hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kDecodeThreads), lds, stream, a);
   } else {
     a.sched = nullptr;
@@ -790,7 +806,7 @@ static hipError_t launch_k(DecodeArgs a, size_t lds, hipStream_t stream) {
 }
 
 template <int DT, int D, int G, bool COW, bool GRP = false>
-static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream, int* ticketed) {
   const size_t lds = decode_lds_bytes(DT, D, G, a.part);
   // Matrix-core scores for 16-bit data at G = 8, when a 16-token step stays inside one block
   // and the waves' shares (part / 4) are whole steps. At G <= 4 the VALU dot products measured
@@ -799,39 +815,37 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool kMF = DT != F32 && G == 8 && !GRP;
   const bool mf = kMF && a.bs_log2 >= 4 && a.part % 64 == 0;
   if (a.kv_cached)
-    return mf ? launch_k<DT, D, G, kMF, false, COW, GRP>(a, lds, stream)
-              : launch_k<DT, D, G, false, false, COW, GRP>(a, lds, stream);
-  return mf ? launch_k<DT, D, G, kMF, true, COW, GRP>(a, lds, stream)
-            : launch_k<DT, D, G, false, true, COW, GRP>(a, lds, stream);
+    return mf ? launch_k<DT, D, G, kMF, false, COW, GRP>(a, lds, stream, ticketed)
+              : launch_k<DT, D, G, false, false, COW, GRP>(a, lds, stream, ticketed);
+  return mf ? launch_k<DT, D, G, kMF, true, COW, GRP>(a, lds, stream, ticketed)
+            : launch_k<DT, D, G, false, true, COW, GRP>(a, lds, stream, ticketed);
 }
 
 // group: the rows of a workgroup (query heads per KV head, times the members of a fork group)
 template <int DT, int D, bool COW, bool GRP = false>
-static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t stream) {
+static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t stream,
+                            int* ticketed) {
   switch (group) {
-    case 1: return launch_t<DT, D, 1, COW, GRP>(a, stream);
-    case 2: return launch_t<DT, D, 2, COW, GRP>(a, stream);
-    case 4: return launch_t<DT, D, 4, COW, GRP>(a, stream);
+    case 1: return launch_t<DT, D, 1, COW, GRP>(a, stream, ticketed);
+    case 2: return launch_t<DT, D, 2, COW, GRP>(a, stream, ticketed);
+    case 4: return launch_t<DT, D, 4, COW, GRP>(a, stream, ticketed);
     case 8:
-      if constexpr (D <= 128) return launch_t<DT, D, 8, COW, GRP>(a, stream);
+      if constexpr (D <= 128) return launch_t<DT, D, 8, COW, GRP>(a, stream, ticketed);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT, bool COW, bool GRP = false>
-static hipError_t launch_d(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
+static hipError_t launch_d(const DecodeArgs& a, int head_dim, int group, hipStream_t stream,
+                            int* ticketed) {
   switch (head_dim) {
-    case 64: return launch_g<DT, 64, COW, GRP>(a, group, stream);
-    case 128: return launch_g<DT, 128, COW, GRP>(a, group, stream);
-    case 256: return launch_g<DT, 256, COW, GRP>(a, group, stream);
+    case 64: return launch_g<DT, 64, COW, GRP>(a, group, stream, ticketed);
+    case 128: return launch_g<DT, 128, COW, GRP>(a, group, stream, ticketed);
+    case 256: return launch_g<DT, 256, COW, GRP>(a, group, stream, ticketed);
     default: return hipErrorInvalidValue;
   }
 }
-
-// The per-partition pass of launches with copy-on-write sources (decode_step.hip).
-hipError_t launch_decode_partitions_cow(const DecodeArgs& a, int kv_dtype, int head_dim,
-                                        int group, hipStream_t stream);
 
 }  // namespace pkv
 

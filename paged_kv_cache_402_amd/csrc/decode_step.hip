@@ -6,11 +6,11 @@
 namespace pkv {
 
 hipError_t launch_decode_partitions_cow(const DecodeArgs& a, int kv_dtype, int head_dim,
-                                        int group, hipStream_t stream) {
+                                        int group, hipStream_t stream, int* ticketed) {
   switch (kv_dtype) {
-    case F32: return launch_d<F32, true>(a, head_dim, group, stream);
-    case F16: return launch_d<F16, true>(a, head_dim, group, stream);
-    case BF16: return launch_d<BF16, true>(a, head_dim, group, stream);
+    case F32: return launch_d<F32, true>(a, head_dim, group, stream, ticketed);
+    case F16: return launch_d<F16, true>(a, head_dim, group, stream, ticketed);
+    case BF16: return launch_d<BF16, true>(a, head_dim, group, stream, ticketed);
     default: return hipErrorInvalidValue;
   }
 }

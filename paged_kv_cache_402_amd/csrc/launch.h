@@ -84,13 +84,20 @@ void decode_timeline(uint32_t** buf, int* cap);
 size_t decode_lds_bytes(int kv_dtype, int head_dim, int group, int part);
 
 // Launches the per-partition kernel (grid: Hkv x pmax x B, or Hkv x work_items in one
-// dimension when a work list is given).
+// dimension when a work list is given). With `ticketed` non-null nothing is launched:
+// *ticketed receives how many units of a work-list launch with these arguments would be
+// handed out by ticket (those at the end of the list; 0 when none would).
 hipError_t launch_decode_partitions(const DecodeArgs& a, int kv_dtype, int head_dim, int group,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int* ticketed = nullptr);
+// The per-partition pass of launches with copy-on-write sources (DecodeArgs::cow_src set;
+// decode_step.hip). launch_decode_partitions forwards such launches here.
+hipError_t launch_decode_partitions_cow(const DecodeArgs& a, int kv_dtype, int head_dim,
+                                        int group, hipStream_t stream, int* ticketed = nullptr);
 // The same over fork groups (DecodeArgs::groups set; decode_groups.hip); rows = query heads
 // per KV head x group size.
 hipError_t launch_decode_partitions_groups(const DecodeArgs& a, int kv_dtype, int head_dim,
-                                           int rows, hipStream_t stream);
+                                           int rows, hipStream_t stream,
+                                           int* ticketed = nullptr);
 // Launches the partition merge (grid: Hq x B); only multi-partition sequences do work.
 hipError_t launch_decode_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream);
 

@@ -116,6 +116,46 @@ def decode_work_list(seq_lens, max_blocks_per_seq: int, block_size: int,
     return items
 
 
+LAUNCH_KINDS = {"plain": 0, "copy_on_write": 1, "fork_groups": 2}
+
+
+def decode_ticketed_items(kv_dtype: torch.dtype, head_dim: int, num_q_heads: int,
+                          num_kv_heads: int, block_size: int, partition_size: int,
+                          list_len: int, kind: str = "plain", group_size: int = 1) -> int:
+    """Items at the end of a work list of list_len items that a launch with an initialised
+    workspace hands out by ticket on the current device (pkv_decode_ticketed_items). kind:
+    "plain" (the _list, _append, _shared and plain calls), "copy_on_write" (the _step calls)
+    or "fork_groups" (the fork-group step, with its group_size)."""
+    if kv_dtype not in KV_DTYPES:
+        raise ValueError("kv_dtype must be float32, float16 or bfloat16")
+    if kind not in LAUNCH_KINDS:
+        raise ValueError("kind must be one of %s" % ", ".join(LAUNCH_KINDS))
+    return check(lib.pkv_decode_ticketed_items(KV_DTYPES[kv_dtype], head_dim, num_q_heads,
+                                               num_kv_heads, block_size, partition_size,
+                                               int(list_len), LAUNCH_KINDS[kind],
+                                               int(group_size)),
+                 "decode_ticketed_items")
+
+
+def decode_work_list_private_tail(work_list, block_tables, seq_lens, block_size: int,
+                                  num_blocks: int, partition_size: int, tail_items: int):
+    """A host work list (pkv_decode_work_list) reordered so that its last tail_items items
+    (from decode_ticketed_items) read no block another item reads, where it has private items
+    to spare (pkv_decode_work_list_private_tail). Returns (list, shared items moved out of the
+    tail); the input is not modified."""
+    tab = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if tab.ndim != 2 or lens.shape != (tab.shape[0],):
+        raise ValueError("block_tables must be [B][W] and seq_lens [B]")
+    items = np.array(np.asarray(work_list, dtype=np.int32).reshape(-1), copy=True)
+    P_i32 = ctypes.POINTER(ctypes.c_int32)
+    moved = check(lib.pkv_decode_work_list_private_tail(
+        tab.ctypes.data_as(P_i32), lens.ctypes.data_as(P_i32), tab.shape[0], tab.shape[1],
+        block_size, num_blocks, partition_size, int(tail_items), items.ctypes.data_as(P_i32),
+        items.shape[0]), "decode_work_list_private_tail")
+    return items, moved
+
+
 def decode_work_list_packed(seq_lens, max_blocks_per_seq: int, block_size: int,
                             partition_size: int = DEFAULT_PARTITION, pack_tokens: int = 64):
     """Host work list with the partitions of at most pack_tokens tokens packed four to a

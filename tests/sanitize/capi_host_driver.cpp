@@ -40,14 +40,33 @@ static void check_decode_args(const DecodeArgs& a) {
   CHECK(a.work == nullptr || a.work_items > 0);
   CHECK(a.pmax <= 1 || (a.ws_ml != nullptr && a.ws_acc != nullptr));
 }
-hipError_t launch_decode_partitions(const DecodeArgs& a, int, int, int group, hipStream_t) {
+// the occupancy query of pkv_decode_ticketed_items: no kernel, a made-up resident count
+static hipError_t ticket_query(const DecodeArgs& a, int* ticketed) {
+  CHECK(a.work_items > 0 && a.num_kv_heads > 0);
+  const int units = a.num_kv_heads * a.work_items;
+  *ticketed = units > 3 * 512 / 2 ? 256 : 0;
+  return hipSuccess;
+}
+hipError_t launch_decode_partitions(const DecodeArgs& a, int, int, int group, hipStream_t,
+                                    int* ticketed) {
+  if (ticketed) return ticket_query(a, ticketed);
   check_decode_args(a);
   CHECK(group == a.num_q_heads / a.num_kv_heads);
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_decode_partitions_cow(const DecodeArgs& a, int, int, int group, hipStream_t,
+                                        int* ticketed) {
+  CHECK(ticketed != nullptr);   // capi reaches the copy-on-write kernels directly only to query
+  CHECK(group == a.num_q_heads / a.num_kv_heads);
+  return ticket_query(a, ticketed);
+}
 hipError_t launch_decode_partitions_groups(const DecodeArgs& a, int, int head_dim, int rows,
-                                           hipStream_t) {
+                                           hipStream_t, int* ticketed) {
+  if (ticketed) {
+    CHECK(rows == a.group_size * a.group_heads);
+    return ticket_query(a, ticketed);
+  }
   check_decode_args(a);
   CHECK(a.groups != nullptr && a.num_groups > 0 && a.group_size >= 1);
   CHECK(a.group_heads == a.num_q_heads / a.num_kv_heads);
@@ -144,6 +163,26 @@ static void work_lists(const Batch& t) {
     const int policy = pkv_decode_kv_policy(t.tables.data(), t.lens.data(), t.B, t.W, t.bs, t.NB,
                                             items.data(), n, part == 0 ? 512 : part);
     if (part == 0 || part % t.bs == 0) CHECK(policy == PKV_KV_STREAM || policy == PKV_KV_CACHED);
+    // the private tail: a permutation of the list, whatever the tail
+    std::vector<int32_t> re(items.begin(), items.begin() + n);
+    const int tail = choose<int>({0, 1, pick(0, n + 3), n, -1});
+    const int moved = pkv_decode_work_list_private_tail(t.tables.data(), t.lens.data(), t.B, t.W,
+                                                        t.bs, t.NB, part, tail, re.data(), n);
+    CHECK(moved <= std::max(tail, 0));
+    if (moved == 0) CHECK(std::equal(re.begin(), re.end(), items.begin()));
+    std::vector<int32_t> a(items.begin(), items.begin() + n), b2(re);
+    std::sort(a.begin(), a.end());
+    std::sort(b2.begin(), b2.end());
+    CHECK(a == b2);
+  }
+  {
+    const int hkv = choose<int>({1, 8, 40, 0});
+    const int ti = pkv_decode_ticketed_items(choose<int>({PKV_F16, PKV_BF16, PKV_F32, 9}),
+                                             choose<int>({64, 128, 256, 100}),
+                                             hkv * choose<int>({1, 2, 4, 8, 3}), hkv, t.bs,
+                                             choose<int>({0, 512, 2048, 48}), pick(-1, 5000),
+                                             pick(-1, 3), choose<int>({1, 2, 4, 0}));
+    CHECK(ti <= 5000);
   }
   int rows = -1;
   const int pack = choose<int>({0, 8, 16, 64, 256, 1000});

@@ -388,7 +388,8 @@ def _sampled_reference(case, q, k, v, seqs):
 @pytest.mark.parametrize("which", ["llama2_7b_mha", "llama3_8b_gqa_prefix", "long_context_splitk"])
 def test_full_size_sampled(which, form):
     """form "bench" is the benchmark's launch exactly as timed: the default partition for the
-    shapes, the host work list, every sequence's newest K/V row (fresh values) stored by the
+    shapes, the host work list with its ticketed tail made private, an initialised workspace
+    (late units by ticket), every sequence's newest K/V row (fresh values) stored by the
     per-partition pass itself, then the merge as its own launch, into an output of the KV
     dtype; the reference reads the caches the pass leaves. "bench_f32out": the same launches
     into an fp32 output (the arithmetic before the final rounding). "grid512": the one-call
@@ -403,14 +404,21 @@ def test_full_size_sampled(which, form):
         B, Hq, D = q.shape
         W, bs, Hkv, dt = case.block_tables.shape[1], case.block_size, case.num_kv_heads, case.dtype
         part = pk.default_partition(B, Hq, Hkv, D, bs, W)
-        work = i32(pk.decode_work_list(case.seq_lens, W, bs, part))
+        need = pk.decode_workspace_bytes(B, Hq, W, bs, D, part)
+        items = pk.decode_work_list(case.seq_lens, W, bs, part)
+        if need:    # late units are ticketed only from an initialised workspace
+            tail = pk.decode_ticketed_items(TORCH_DT[dt], D, Hq, Hkv, bs, part, items.shape[0])
+            items, _ = pk.decode_work_list_private_tail(items, case.block_tables, case.seq_lens,
+                                                        bs, case.num_blocks, part, tail)
+        work = i32(items)
         k_new = gen.device_normal((B, Hkv, D), dt, 4030, "cuda")
         v_new = gen.device_normal((B, Hkv, D), dt, 4031, "cuda")
         odt = TORCH_DT[dt] if form == "bench" else torch.float32
         out = torch.full((B, Hq, D), float("nan"), dtype=odt, device="cuda")
         tables, lens_d = i32(case.block_tables), i32(case.seq_lens)
-        ws = torch.empty(max(1, pk.decode_workspace_bytes(B, Hq, W, bs, D, part)),
-                         dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+        if need:
+            pk.decode_workspace_init(ws)
         policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, bs, case.num_blocks)
         assert policy == pk.KV_STREAM          # no batch here mostly re-reads shared blocks
         pk.paged_attention_partitions_append(out, q, k_new, v_new, k, v, tables, lens_d,
@@ -1176,3 +1184,94 @@ def test_scheduled_units_are_each_taken_once_and_bitwise_static(shape):
         assert np.array_equal(taken, np.arange(units)), rep
         assert (rec[:, 4] != np.arange(units)).any()        # the scheduling word was used
     assert np.isfinite(want.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("kind", ["plain", "copy_on_write", "fork_groups", "matrix_core_g8",
+                                  "short"])
+def test_ticketed_items_match_the_launch(kind):
+    """pkv_decode_ticketed_items against the launch itself. Over a workspace that was never
+    initialised every late workgroup still adds one to the scheduling word (and keeps its
+    static unit), so after one launch the word holds how many units were ticketed; the query,
+    in items, is that count over the KV heads rounded up. A list of no more units than fit on
+    the device at once tickets nothing: the query says 0 and the word stays 0."""
+    import paged_kv_cache_402_amd as pk
+    rng = np.random.default_rng(7400)
+    Hkv, D, bs, dt = 8, 128, 16, "bf16"
+    G = 8 if kind == "matrix_core_g8" else 4
+    nseq = 40 if kind == "short" else 700
+    lens = [int(x) for x in rng.integers(2, 700, size=nseq)]
+    case = gen.make_case("tix", rng, lens, G * Hkv, Hkv, D, bs, dt, values=False)
+    B, Hq, W = nseq, G * Hkv, case.block_tables.shape[1]
+    part = 512 if kind == "matrix_core_g8" else 256
+    shape4 = (case.num_blocks, Hkv, bs, D)
+    k = gen.device_normal(shape4, dt, 7401, "cuda")
+    v = gen.device_normal(shape4, dt, 7402, "cuda")
+    q = gen.device_normal((B, Hq, D), dt, 7403, "cuda")
+    k_new = gen.device_normal((B, Hkv, D), dt, 7404, "cuda")
+    v_new = gen.device_normal((B, Hkv, D), dt, 7405, "cuda")
+    tables, lns = i32(case.block_tables), i32(case.seq_lens)
+    items = pk.decode_work_list(case.seq_lens, W, bs, part)
+    work = i32(items)
+    need = pk.decode_workspace_bytes(B, Hq, W, bs, D, part)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")        # never initialised
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    cow = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lkind, gsize = "plain", 1
+    if kind == "copy_on_write":
+        lkind = "copy_on_write"
+        pk.paged_attention_partitions_step(out, q, k_new, v_new, cow, k, v, tables, lns,
+                                           case.scale, partition_size=part, workspace=ws,
+                                           work_list=work)
+    elif kind == "fork_groups":
+        lkind, gsize = "fork_groups", 1
+        groups = torch.arange(B, dtype=torch.int32, device="cuda").view(B, 1)
+        pk.paged_attention_partitions_step_groups(out, q, k_new, v_new, cow, k, v, tables, lns,
+                                                  case.scale, groups, work,
+                                                  partition_size=part, workspace=ws)
+    else:
+        pk.paged_attention_partitions(out, q, k, v, tables, lns, case.scale,
+                                      partition_size=part, workspace=ws, work_list=work)
+    torch.cuda.synchronize()
+    count = _sched_word(ws) & 0xFFFFFFFF
+    assert _sched_word(ws) >> 32 == 0
+    got = pk.decode_ticketed_items(torch.bfloat16, D, Hq, Hkv, bs, part, items.shape[0], lkind,
+                                   gsize)
+    if kind == "short":
+        assert items.shape[0] * Hkv < 1024 and count == 0 and got == 0
+    else:
+        assert count > 0
+        assert got == -(-count // Hkv), (count, got)
+
+
+def test_private_tail_list_is_bitwise_the_default_list():
+    """The GQA 8B batch-256 workload with a 512-token shared prefix, at its 2048-token
+    partitions, as the benchmark launches it (initialised workspace, late units by ticket):
+    the reordered list moves the 12 partition-0 items (which read the prefix) out of the
+    ticketed tail, and its outputs are bitwise those of the default list."""
+    import paged_kv_cache_402_amd as pk
+    case = gen.llama3_8b_gqa_prefix_case(values=False)
+    q, k, v = _device_values(case, 4020)
+    B, Hq, D = q.shape
+    W, bs, Hkv, dt = case.block_tables.shape[1], case.block_size, case.num_kv_heads, case.dtype
+    part = pk.default_partition(B, Hq, Hkv, D, bs, W)
+    assert part == 2048
+    items = pk.decode_work_list(case.seq_lens, W, bs, part)
+    tail = pk.decode_ticketed_items(torch.bfloat16, D, Hq, Hkv, bs, part, items.shape[0])
+    assert tail > 0
+    moved_items, moved = pk.decode_work_list_private_tail(items, case.block_tables,
+                                                          case.seq_lens, bs, case.num_blocks,
+                                                          part, tail)
+    assert moved > 0 and ((moved_items[-tail:] & 0xFFFF) >= 1).all()
+    tables, lns = i32(case.block_tables), i32(case.seq_lens)
+    need = pk.decode_workspace_bytes(B, Hq, W, bs, D, part)
+    outs = []
+    for lst in (items, moved_items):
+        ws = pk.decode_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        pk.paged_attention_partitions(out, q, k, v, tables, lns, case.scale, partition_size=part,
+                                      workspace=ws, work_list=i32(lst))
+        pk.paged_attention_reduce(out, lns, bs, W, ws, partition_size=part)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).clone())
+    assert torch.equal(outs[0], outs[1])
+    assert np.isfinite(outs[0].view(torch.bfloat16).float().cpu().numpy()).all()
