@@ -852,12 +852,11 @@ def main():
     bytes_ = byte_model(case, part)
     work, members, pp, items = None, None, 0, None
     groups = None
-    # no workspace: no sequence spans two partitions and the merge pass has nothing to do
-    ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
-                                         case.block_size, case.head_dim, part)
     # the ticketed tail made private (late units are ticketed only over an initialised
-    # workspace)
-    reorder_tail = ws_bytes > 0 and not args.no_sched and not args.keep_tail
+    # workspace; the list and fork grids keep this partition)
+    reorder_tail = (pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
+                                              case.block_size, case.head_dim, part) > 0
+                    and not args.no_sched and not args.keep_tail)
     moved = 0
     kind = "copy_on_write" if st["pairs"] is not None and args.append == "fused" else "plain"
     if args.grid == "forks":
@@ -936,6 +935,9 @@ def main():
         policy = pk.decode_kv_policy(case.block_tables, case.seq_lens, case.block_size,
                                      case.num_blocks, work_list=items, partition_size=part)
     log("KV read policy: %s" % ("cached" if policy == pk.KV_CACHED else "stream"))
+    # no workspace: no sequence spans two partitions and the merge pass has nothing to do
+    ws_bytes = pk.decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.table_width,
+                                         case.block_size, case.head_dim, part)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     if ws_bytes and not args.no_sched:
         pk.decode_workspace_init(ws)     # list launches hand out late units from its header
