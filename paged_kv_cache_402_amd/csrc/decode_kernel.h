@@ -275,6 +275,46 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
 #pragma unroll
     for (int i = 0; i < K::NLK; ++i)
       qv[g][i] = load16(qrow(g) + (size_t)(kc + i * K::LK) * 16);
+  // fork group with few enough rows (HOIST): each row's own new token costs no round trip of
+  // its own. Its K row (k_new; the address needs only the member) is loaded beside the query
+  // slices and scored before the K pass; its V row is loaded with the first V round. The rows'
+  // new K and V rows for their cache slots are spread over the lanes of one wave (wave 0, or
+  // each wave of a packed row, which has a group of its own), loaded here and stored once the K
+  // pass is done. More rows, or fp32 rows, would take registers enough to cost a wave per
+  // SIMD: they load their own rows after each pass instead.
+  constexpr bool HOIST = GRP && DT != F32 && G <= 4 && G * K::NLK <= 8;
+  constexpr int OWN_PER_LANE = (2 * G * K::C + 63) / 64;    // 16-byte pieces, K rows then V
+  u32x4 kown[HOIST ? G : 1][K::NLK];
+  u32x4 own_put[HOIST ? OWN_PER_LANE : 1];
+  // row g's new K or V row (g known at compile time: the register arrays are never indexed
+  // at run time, which would send them to scratch memory)
+  auto own_row = [&](int g, bool isv) -> const unsigned char* {
+    const unsigned char* base = (const unsigned char*)(isv ? a.v_new : a.k_new);
+    return base + ((size_t)max(rowseq[g], 0) * a.num_kv_heads + kvh) * K::RB;
+  };
+  // piece j of this lane in the spread of the 2G own rows: row j * RPP + lane / C of them
+  // (the K rows, then the V rows), column lane % C
+  constexpr int RPP = 64 / K::C;                             // rows per pass of the lanes
+  const bool own_wave = packed || wave == 0;                 // the wave that stores them
+  // (a fork-group launch always carries k_new and v_new; the test keeps a launch without
+  // them from reading through null)
+  if constexpr (HOIST) if (a.k_new != nullptr && a.v_new != nullptr) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < K::NLK; ++i)
+        kown[g][i] = load16(own_row(g, false) + (size_t)(kc + i * K::LK) * 16);
+#pragma unroll
+    for (int j = 0; j < OWN_PER_LANE; ++j) {
+      own_put[j] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int rr = 0; rr < RPP; ++rr) {
+        const int r = j * RPP + rr;
+        if (own_wave && r < 2 * G && lane / K::C == rr)
+          own_put[j] = load16(own_row(r % G, r >= G) + (size_t)(lane % K::C) * 16);
+      }
+    }
+  }
   const int cap = a.max_blocks << a.bs_log2;
   int L = a.seq_lens[lead];
   L = L < 0 ? 0 : (L > cap ? cap : L);
@@ -386,6 +426,18 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       if (k == (jb >> 6) && lane == (jb & 63)) ids[k] = cow;
   }
 
+
+  // fork group (HOIST): each row's own score, from the K row loaded with the query slices
+  float so[HOIST ? G : 1];
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < K::NLK; ++i) acc = dot16<DT>(qv[g][i], kown[g][i], acc);
+      so[g] = rowseq[g] >= 0 ? group_sum<K::LK>(acc) * a.scale_log2 : -INFINITY;
+    }
+  }
 
   // ---- K pass over the wave's share: scores (log2 units) -> LDS, running max ----
   float m[G];
@@ -514,7 +566,29 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       }
     }
   }
-  if constexpr (GRP) {
+  if constexpr (HOIST) {
+    // each row's own score into the slot of its new token (the pass above left -inf there)
+    if (fused && last >= c0 && last < c0 + nw) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], so[g]);
+      if (lane == 0) lds_store_n<G>(s_sc + (last - c0) * G, so);
+    }
+    // the members' new K and V rows into their cache slots: a member's first row only, so
+    // each is stored once (rblk: -1 unless this partition holds the new token)
+#pragma unroll
+    for (int j = 0; j < OWN_PER_LANE; ++j)
+#pragma unroll
+      for (int rr = 0; rr < RPP; ++rr) {
+        const int r = j * RPP + rr;
+        if (own_wave && r < 2 * G && lane / K::C == rr && rblk[r % G] >= 0 &&
+            (r % G) % a.group_heads == 0) {
+          unsigned char* slot = (unsigned char*)(r >= G ? a.v_cache : a.k_cache) +
+                                kvh * head_bytes + (size_t)rblk[r % G] * block_bytes +
+                                (size_t)(last & bs_mask) * K::RB;
+          store16(slot + (size_t)(lane % K::C) * 16, own_put[j]);
+        }
+      }
+  } else if constexpr (GRP) {
     // each row's own new token: its score against the member's K row from k_new, into the
     // slot of that position (the pass above left -inf there)
     if (fused && last >= c0 && last < c0 + nw) {
@@ -572,6 +646,19 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
       }
     }
   };
+  // fork group (HOIST): the own rows' V rows, loaded with the first V round by the lanes that
+  // add them (the first row group of the wave that holds the new token)
+  const bool own_v = HOIST && fused && last >= c0 && last < c0 + nw && vr == 0;
+  u32x4 vown[HOIST ? G : 1][K::NLV];
+  if constexpr (HOIST) {
+    if (own_v) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < K::NLV; ++i)
+          vown[g][i] = load16(own_row(g, true) + (size_t)(vc + i * K::LV) * 16);
+    }
+  }
   load_v(0);
 
   // ---- probabilities 2^(s - max) in place, once per (token, head); their sum ----
@@ -602,6 +689,25 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < K::ACC; ++e) acc[g][e] = 0.f;
+  if constexpr (HOIST) {
+    // each row's own new token first: its weight times the member's V row
+    if (own_v) {
+      float pg[G];
+      lds_load_n<G>(s_sc + (last - c0) * G, pg);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (rowseq[g] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < K::NLV; ++i) {
+          float f[K::PER16];
+          widen<DT>(vown[g][i], f);
+#pragma unroll
+          for (int e = 0; e < K::PER16; ++e)
+            acc[g][i * K::PER16 + e] = __builtin_fmaf(pg[g], f[e], acc[g][i * K::PER16 + e]);
+        }
+      }
+    }
+  }
   for (int g0 = 0; g0 < ngv; g0 += K::UV) {
     if (g0 > 0) load_v(g0);
 #pragma unroll
@@ -633,7 +739,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_partition_kernel(
     }
   }
 
-  if constexpr (GRP) {
+  if constexpr (GRP && !HOIST) {
     // each row's own new token: its weight times the member's V row from v_new, once per
     // column (the lanes of the first row group)
     if (fused && last >= c0 && last < c0 + nw && vr == 0) {
