@@ -66,16 +66,18 @@ def _work(P, glens, W, bs, part, form):
     return (i32(lst), rows)
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,bs,part,form,group", [
-    ("bf16", 32, 8, 16, 512, "list", 2),      # 4 heads x 2 members: 8 rows
-    ("f16", 40, 40, 32, 2048, "packed", 4),   # MHA, 4 members
-    ("f32", 8, 4, 8, 64, "list", 4),          # 2 heads x 4 members, many partitions
-    ("bf16", 16, 16, 16, 256, "packed", 8),   # MHA, 8 members (groups of 4 padded)
-    ("f16", 32, 8, 16, 512, "list", 1),       # one member: the per-sequence rows
-    ("bf16", 64, 8, 64, 1024, "list", 1),     # 8 query heads per KV head, one member
-    ("f32", 16, 8, 16, 256, "packed", 2),     # head_dim 256 (f32 rows of 1 KiB), 2 x 2 rows
+@pytest.mark.parametrize("dtype,hq,hkv,bs,part,form,group,hd", [
+    ("bf16", 32, 8, 16, 512, "list", 2, 0),      # 4 heads x 2 members: 8 rows
+    ("f16", 40, 40, 32, 2048, "packed", 4, 0),   # MHA, 4 members
+    ("f32", 8, 4, 8, 64, "list", 4, 0),          # 2 heads x 4 members, many partitions
+    ("bf16", 16, 16, 16, 256, "packed", 8, 0),   # MHA, 8 members (groups of 4 padded)
+    ("f16", 32, 8, 16, 512, "list", 1, 0),       # one member: the per-sequence rows
+    ("bf16", 64, 8, 64, 1024, "list", 1, 0),     # 8 query heads per KV head, one member
+    ("f32", 16, 8, 16, 256, "packed", 2, 0),     # head_dim 256 (f32 rows of 1 KiB), 2 x 2 rows
+    ("bf16", 16, 8, 16, 256, "list", 2, 64),     # head_dim 64, 2 heads x 2 members
+    ("f16", 8, 8, 16, 512, "packed", 2, 256),    # head_dim 256 16-bit rows, 2 members
 ])
-def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form, group):
+def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form, group, hd):
     """Prompts of many lengths (a partial last block, a full one, empty, longer than a
     partition) forked into 1-4 branches, then one token each. The groups come from the
     planner; the group step must leave the per-sequence fused step's caches bit for bit, and
@@ -83,7 +85,7 @@ def test_group_step_matches_the_per_sequence_step(dtype, hq, hkv, bs, part, form
     NaN, so a read of a row before it is written would show."""
     P = pk()
     rng = np.random.default_rng(90 + group + hq)
-    d = 128 if dtype != "f32" else (256 if hq == 16 else 64)
+    d = hd or (128 if dtype != "f32" else (256 if hq == 16 else 64))
     prompts = [3 * bs - 3, 2 * bs, part + 5, 1, 0, bs + 1, 2 * part - 1, 7]
     branches = [4, 3, 2, 1, 2, 4, 3, 1]
     nb, kd, vd, seqs, slots, pairs, cow_src, tables, lens, W = _forked_batch(
