@@ -51,6 +51,10 @@ DEFAULT_PACK = {"llama13b_longtail": 256, "llama3_8b_short_batch": 48}
 # the branches of long forked prompts 293.9 -> 195.8 us in fork groups; a 4096-token document
 # shared by 256 sequences 413 -> 118.5 us with the shared-prefix pass
 DEFAULT_GRID = {"llama13b_fork_long": "forks", "llama3_8b_long_shared_prefix": "shared"}
+# partition size of the (workload, grid) pairs whose measured best is not the library's default:
+# the long-prompt fork groups, 1680 workgroups at 2048 tokens (1.6 resident rounds, a long
+# drain), 192.9 -> 182.8 us at 1024 (1536: 184.3 us)
+DEFAULT_PARTITION = {("llama13b_fork_long", "forks"): 1024}
 FORKED = {"llama13b_longtail": "llama13b_longtail_case",
           "llama13b_fork_long": "llama13b_fork_long_case"}
 
@@ -62,7 +66,10 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_gqa_prefix", choices=BENCH_WORKLOADS)
     p.add_argument("--partition", type=int, default=0,
-                   help="tokens per context partition (0: the library's default for the shapes)")
+                   help="tokens per context partition (0: the workload's measured best, %s, else "
+                        "the library's default for the shapes)"
+                        % ", ".join("%s with --grid %s %d" % (w, g, v)
+                                    for (w, g), v in DEFAULT_PARTITION.items()))
     p.add_argument("--grid", choices=("shared", "list", "full", "forks"), default=None,
                    help="shared: partitions that a group of sequences shares run once for the "
                         "whole group on the matrix cores, the rest over a work list; list: "
@@ -846,9 +853,9 @@ def main():
     log("setting up %s" % args.workload)
     st = build_state(args.workload, pk, gen, torch, dev)
     case = st["case"]
-    part = args.partition or pk.default_partition(case.num_seqs, case.num_q_heads,
-                                                  case.num_kv_heads, case.head_dim,
-                                                  case.block_size, case.table_width)
+    part = (args.partition or DEFAULT_PARTITION.get((args.workload, args.grid))
+            or pk.default_partition(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                    case.head_dim, case.block_size, case.table_width))
     bytes_ = byte_model(case, part)
     work, members, pp, items = None, None, 0, None
     groups = None
