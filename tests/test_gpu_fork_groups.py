@@ -252,9 +252,10 @@ def test_group_step_long_tail_parallel_sampling():
 
 def test_group_step_long_prompt_forks_full_size():
     """The long-prompt fork workload at full size (32 prompts x 4 branches of mean 1432 tokens,
-    40 MHA heads, fp16, block 32) in the launch the bench times (the groups' plain list,
-    2048-token partitions, the merge): caches bitwise those of the per-sequence step, outputs
-    within fp32 rounding of it, sampled sequences against the oracle."""
+    40 MHA heads, fp16, block 32) in the launch the bench times (the groups' plain list with
+    its ticketed tail made private, 1024-token partitions, late units by ticket, the merge):
+    caches bitwise those of the per-sequence step, outputs within fp32 rounding of it, sampled
+    sequences against the oracle."""
     P = pk()
     c = gen.llama13b_fork_long_case(values=False)
     nb, bs, H, d, B = c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim, c.num_seqs
@@ -271,7 +272,7 @@ def test_group_step_long_prompt_forks_full_size():
     kd, vd = gen.device_normal(shape, "f16", 91, "cuda"), gen.device_normal(shape, "f16", 92, "cuda")
     q = gen.device_normal((B, H, d), "f16", 93, "cuda")
     k_new, v_new = gen.device_normal((B, H, d), "f16", 94, "cuda"), gen.device_normal((B, H, d), "f16", 95, "cuda")
-    part = 2048
+    part = 1024
     k1, v1 = kd.clone(), vd.clone()
     o1 = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
     P.paged_attention_decode_step(o1, q, k_new, v_new, i32(cow_src), k1, v1, i32(tables),
@@ -282,9 +283,12 @@ def test_group_step_long_prompt_forks_full_size():
     ws = torch.empty(P.decode_workspace_bytes(B, H, c.table_width, bs, d, part), dtype=torch.uint8,
                      device="cuda")
     P.decode_workspace_init(ws)          # the bench's ticketed late units
+    lst = P.decode_work_list(glens, c.table_width, bs, part)
+    tail = P.decode_ticketed_items(torch.float16, d, H, H, bs, part, lst.shape[0], "fork_groups",
+                                   c.branches)
+    lst, _ = P.decode_work_list_private_tail(lst, tables[groups[:, 0]], glens, bs, nb, part, tail)
     P.paged_attention_decode_step_groups(o2, q, k_new, v_new, i32(cow_src), k2, v2, i32(tables),
-                                         i32(lens), c.scale, i32(groups),
-                                         i32(P.decode_work_list(glens, c.table_width, bs, part)),
+                                         i32(lens), c.scale, i32(groups), i32(lst),
                                          partition_size=part, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
